@@ -1,0 +1,179 @@
+/*
+ * nvpaged — paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the hot path of a nano-vLLM style engine: the store of new K/V rows
+ * into a block-paged cache, paged GQA decode attention and packed varlen causal
+ * prefill attention that reads cached prefix blocks, plus the host-side metadata
+ * builders that produce slot_mapping and cu_seqlens.
+ *
+ * Sources for the operations (web pages on nano-vLLM):
+ *   [walkthrough]  the xingyun3d.csdn.net article on nano-vllm, sections
+ *                  五 "KV Block 管理", 六 "模型执行", 七 "后端执行（cuda 算子）",
+ *                  八 "序列与上下文";
+ *   [paging]       the gsyq.cn article "项目概述：为什么我们需要关注 LLM 推理引擎？",
+ *                  sections 4.1 and 5.3;
+ *   [deep dive]    "万字深度解析 Nano-vLLM" (chenxutan.com), sections 1.2 and 3.2.1;
+ *   [summary]      the gitcode.csdn.net nano-vLLM article, section 三.4.
+ *
+ * Common conventions
+ *   - Cache layout: k_cache and v_cache are each one contiguous device array
+ *     [num_blocks, block_size, num_kv_heads, head_dim] in the element dtype.
+ *     A slot is the row index into that array viewed as
+ *     [num_blocks * block_size, num_kv_heads, head_dim], i.e.
+ *     slot = physical_block * block_size + offset ([paging] 4.1, [walkthrough] 八).
+ *   - block_tables: int32 [num_seqs, max_blocks_per_seq], row-major; entry i of
+ *     row s is the physical block holding tokens i*block_size .. of sequence s.
+ *     Entries past a sequence's last used block are never read.
+ *   - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads)
+ *     ([deep dive] 3.2.1).
+ *   - Supported: dtype NV_F32 or NV_BF16 (all tensors of a call share it),
+ *     head_dim 64 or 128, block_size a positive multiple of 16,
+ *     num_q_heads a multiple of num_kv_heads with at most 8 query heads per KV head.
+ *   - Every pointer is caller-owned.  Device pointers must be device memory (for
+ *     example from a PyTorch tensor); host pointers are ordinary host memory.
+ *     The library keeps no state between calls and allocates no memory.
+ *   - GPU entry points enqueue work on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return without synchronising.  Host-checkable argument errors
+ *     are reported before anything is enqueued; a failed launch returns
+ *     NV_ERR_HIP.  Values inside device arrays (slots, block ids, lengths) are
+ *     preconditions and are not checked: out-of-range values are undefined
+ *     behaviour.
+ */
+#ifndef NVPAGED_H
+#define NVPAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nv_status {
+  NV_OK = 0,
+  NV_ERR_INVALID_ARG = -1,          /* null pointer, negative size, inconsistent sizes */
+  NV_ERR_UNSUPPORTED = -2,          /* head_dim / block_size / dtype / group size not built */
+  NV_ERR_WORKSPACE_TOO_SMALL = -3,  /* decode workspace smaller than the size query */
+  NV_ERR_HIP = -4                   /* a HIP launch or runtime call failed */
+} nv_status;
+
+typedef enum nv_dtype {
+  NV_F32 = 0,
+  NV_BF16 = 1
+} nv_dtype;
+
+/* Static, NUL-terminated description of a status code. */
+const char* nv_status_string(nv_status status);
+
+/* ------------------------------------------------------------------------- *
+ * store_kvcache  ([walkthrough] 七; [summary] 三.4)
+ *
+ * Before attention, the step's new K/V rows are copied into the pre-allocated
+ * cache at the slots given by slot_mapping.  Row i of k (and of v) holds
+ * num_kv_heads * head_dim contiguous elements starting at k + i * k_row_stride
+ * elements; the stride lets k and v be views into a fused qkv projection.
+ * slot_mapping[i] == -1 skips row i (padding) and leaves the cache untouched.
+ * The copy is bit-exact.  Non-negative slots must be unique and lie in
+ * [0, num_blocks * block_size).  num_tokens == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+nv_status nv_store_kvcache(const void* k, const void* v,
+                           int64_t k_row_stride, int64_t v_row_stride,
+                           void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t num_blocks, int32_t block_size,
+                           int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * paged decode  ([walkthrough] 七: decode attends cache_seqlens = context_lens
+ * keys through the block table; [deep dive] 1.2: softmax(Q K^T / sqrt(d)) V)
+ *
+ * out[b, h, :] = softmax(softmax_scale * q[b, h, :] . K_b[t, h/g, :]) V_b[t, h/g, :]
+ * over t = 0 .. context_lens[b] - 1, where K_b / V_b are sequence b's rows
+ * gathered through block_tables[b].  context_lens[b] counts the token being
+ * decoded, whose row must already be stored.
+ *   q, out: [batch, num_q_heads, head_dim] contiguous, dtype elements.
+ *   context_lens: int32 [batch], each in [1, max_blocks_per_seq * block_size]
+ *     and <= max_context_len (a host-side bound used to size the split work).
+ *   Accumulation is fp32; the output is rounded to the dtype (nearest-even).
+ *   workspace: device memory of at least nv_paged_decode_workspace_size(...)
+ *     bytes (may be NULL when that size is 0).  Its leading counter words must
+ *     be zero before the first call that uses the buffer (allocate it zeroed);
+ *     every completed call leaves them zero again.  Calls that share one
+ *     workspace must be ordered on one stream.
+ *   out must not alias q, the caches or the workspace.  batch == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+size_t nv_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t max_context_len, int32_t block_size,
+                                      int32_t dtype);
+
+nv_status nv_paged_decode(void* out, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len,
+                          int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                          float softmax_scale, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * paged varlen prefill  ([walkthrough] 七: the prefill call takes q, the cache,
+ * cu_seqlens_q/k, max_seqlen_q/k, causal=True and the block table; 八: only the
+ * uncached part of each sequence is computed)
+ *
+ * Sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 (n_s rows)
+ * and keys 0 .. k_s-1 with k_s = cu_seqlens_k[s+1] - cu_seqlens_k[s] >= n_s, all
+ * read from the cache through block_tables[s] (the new rows must already be
+ * stored).  Query row i is the token at position k_s - n_s + i; with causal != 0
+ * it attends keys 0 .. k_s - n_s + i (bottom-right aligned mask), otherwise all
+ * k_s keys.
+ *   q, out: [cu_seqlens_q[num_seqs], num_q_heads, head_dim] contiguous.
+ *   cu_seqlens_q/k: int32 [num_seqs + 1], non-decreasing, starting at 0.
+ *   max_seqlen_q >= every n_s and max_seqlen_k >= every k_s (host-side bounds
+ *   used to size the grid).  Rows of sequences with n_s == 0 are absent.
+ *   out must not alias q or the caches.  num_seqs == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+nv_status nv_paged_prefill(void* out, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           float softmax_scale, int32_t causal, int32_t dtype,
+                           void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Host-side metadata builders ([walkthrough] 七: prepare_decode /
+ * prepare_prefill).  All pointers are HOST memory; nothing touches the GPU.
+ * Every block-table entry they read is validated against num_blocks.
+ * ------------------------------------------------------------------------- */
+
+/* Decode: slot_mapping[b] = slot of position context_lens[b] - 1 (the token
+ * decoded this step); *max_context_len = max_b context_lens[b] (0 if batch == 0). */
+nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch,
+                            int32_t block_size, int32_t num_blocks,
+                            int32_t* slot_mapping, int32_t* max_context_len);
+
+/* Prefill: sequence s has num_cached[s] tokens already in the cache and
+ * num_new[s] new tokens at positions num_cached[s] .. num_cached[s]+num_new[s]-1.
+ * Writes cu_seqlens_q/k ([num_seqs + 1]), the maxima, and the slots of the new
+ * tokens in packed order followed by -1 up to the next multiple of pad_to
+ * (pad_to >= 1).  slot_capacity is the length of slot_mapping; *num_slots
+ * receives the padded count.  Returns NV_ERR_INVALID_ARG if it does not fit. */
+nv_status nv_prepare_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* num_cached, const int32_t* num_new,
+                             int32_t num_seqs, int32_t block_size, int32_t num_blocks,
+                             int32_t pad_to,
+                             int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                             int32_t* max_seqlen_q, int32_t* max_seqlen_k,
+                             int32_t* slot_mapping, int32_t slot_capacity,
+                             int32_t* num_slots);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVPAGED_H */

@@ -1,0 +1,201 @@
+"""Thin Python binding of libnvpaged.so.
+
+The functions carry the C entry points' names and only marshal arguments:
+device tensors become raw pointers, host arrays become int32 buffers, and the
+current torch stream becomes the hipStream_t.  Every step of the path runs in
+the HIP library; nothing here computes attention or copies cache rows.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from . import _native
+
+NV_OK = 0
+NV_F32 = 0
+NV_BF16 = 1
+
+_DTYPES = {torch.float32: NV_F32, torch.bfloat16: NV_BF16}
+
+
+class NvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = _native.load().nv_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+
+
+def _check(fn: str, status: int):
+    if status != NV_OK:
+        raise NvError(fn, status)
+
+
+def nv_status_string(status: int) -> str:
+    return _native.load().nv_status_string(status).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _dev(t: torch.Tensor, name: str, contiguous: bool = True) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_native.c_i32p)
+
+
+# ---------------------------------------------------------------------------
+# store_kvcache
+# ---------------------------------------------------------------------------
+
+def nv_store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """k, v: [N, Hkv, D] (rows may be strided, heads and dims contiguous);
+    caches: [num_blocks, block_size, Hkv, D]; slot_mapping: int32 [N] on the device."""
+    nb, bs, hkv, d = k_cache.shape
+    n = k.shape[0]
+    for name, t in (("k", k), ("v", v)):
+        if t.shape[1:] != (hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name} must be [N, {hkv}, {d}] with contiguous heads")
+    if slot_mapping.dtype != torch.int32 or slot_mapping.numel() != n:
+        raise ValueError("slot_mapping must be int32 with one entry per row")
+    st = _native.load().nv_store_kvcache(
+        _dev(k, "k", False), _dev(v, "v", False), k.stride(0), v.stride(0),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"),
+        n, hkv, d, nb, bs, _dtype_code(k_cache), _stream(stream, k_cache.device))
+    _check("nv_store_kvcache", st)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def nv_paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int,
+                                   head_dim: int, max_context_len: int, block_size: int,
+                                   dtype: int) -> int:
+    return int(_native.load().nv_paged_decode_workspace_size(
+        batch, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, dtype))
+
+
+_ws_cache = {}
+
+
+def decode_workspace(device, nbytes: int) -> Optional[torch.Tensor]:
+    """A zero-initialised workspace of at least nbytes, cached per device.  The decode
+    kernels return its counter words to zero, so the buffer is reusable by later calls
+    ordered on the same stream."""
+    if nbytes == 0:
+        return None
+    key = torch.device(device)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=key)
+        _ws_cache[key] = buf
+    return buf
+
+
+def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, max_context_len: int, softmax_scale: float,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    nb, bs, hkv, d = k_cache.shape
+    batch, hq = q.shape[0], q.shape[1]
+    dt = _dtype_code(k_cache)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
+    if workspace is None:
+        workspace = decode_workspace(k_cache.device, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _native.load().nv_paged_decode(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, "context_lens"), max_context_len, batch, hq, hkv, d, nb, bs,
+        float(softmax_scale), dt, ws_ptr, ws_len, _stream(stream, q.device))
+    _check("nv_paged_decode", st)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def nv_paged_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                     cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
+                     block_tables: torch.Tensor, softmax_scale: float, causal: bool = True,
+                     stream=None) -> None:
+    nb, bs, hkv, d = k_cache.shape
+    hq = q.shape[1]
+    num_seqs = cu_seqlens_q.numel() - 1
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                    ("block_tables", block_tables)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    st = _native.load().nv_paged_prefill(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"),
+        max_seqlen_q, max_seqlen_k, _dev(block_tables, "block_tables"), block_tables.shape[1],
+        num_seqs, hq, hkv, d, nb, bs, float(softmax_scale), int(bool(causal)),
+        _dtype_code(k_cache), _stream(stream, q.device))
+    _check("nv_paged_prefill", st)
+
+
+# ---------------------------------------------------------------------------
+# host metadata
+# ---------------------------------------------------------------------------
+
+def nv_prepare_decode(block_tables, context_lens, block_size: int,
+                      num_blocks: int) -> Tuple[np.ndarray, int]:
+    bt = _i32(block_tables)
+    cl = _i32(context_lens)
+    batch = cl.shape[0]
+    slots = np.empty(batch, dtype=np.int32)
+    mx = ctypes.c_int32(0)
+    st = _native.load().nv_prepare_decode(_ptr(bt), bt.shape[1] if bt.ndim == 2 else 1,
+                                          _ptr(cl), batch, block_size, num_blocks,
+                                          _ptr(slots), ctypes.byref(mx))
+    _check("nv_prepare_decode", st)
+    return slots, int(mx.value)
+
+
+def nv_prepare_prefill(block_tables, num_cached, num_new, block_size: int, num_blocks: int,
+                       pad_to: int = 1):
+    bt = _i32(block_tables)
+    p = _i32(num_cached)
+    n = _i32(num_new)
+    S = n.shape[0]
+    cap = int(-(-int(n.sum()) // pad_to) * pad_to) if S else 0
+    cu_q = np.empty(S + 1, dtype=np.int32)
+    cu_k = np.empty(S + 1, dtype=np.int32)
+    slots = np.empty(max(cap, 1), dtype=np.int32)
+    mq, mk, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    st = _native.load().nv_prepare_prefill(
+        _ptr(bt), bt.shape[1] if bt.ndim == 2 else 1, _ptr(p), _ptr(n), S, block_size,
+        num_blocks, pad_to, _ptr(cu_q), _ptr(cu_k), ctypes.byref(mq), ctypes.byref(mk),
+        _ptr(slots), cap, ctypes.byref(ns))
+    _check("nv_prepare_prefill", st)
+    return cu_q, cu_k, int(mq.value), int(mk.value), slots[:ns.value].copy()

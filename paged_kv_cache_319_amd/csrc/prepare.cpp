@@ -1,0 +1,107 @@
+// Host-side step metadata: slot_mapping and cu_seqlens.
+//
+// Walkthrough (xingyun3d.csdn.net nano-vllm article), section 七: before each
+// forward pass the runner builds, for prefill, the prefix sums cu_seqlens_q/k,
+// max_seqlen_q/k and the physical slot of every newly written token; for
+// decode, each sequence's current length and the slot of its last token.
+// Section 八 defines the slot as the one-dimensional index of the physical row;
+// the gsyq.cn paging article (section 4.1) places token t in logical block
+// t / B at offset t % B.  With the cache viewed as [num_blocks * B, ...] rows,
+// slot = block_tables[s][t / B] * B + t % B.
+#include <stdint.h>
+
+#include "nvpaged.h"
+
+namespace {
+
+// Slot of position t of the sequence whose table row is `row`; -1 on a bad entry.
+int64_t slot_for(const int32_t* row, int32_t width, int32_t t, int32_t block_size,
+                 int32_t num_blocks) {
+  const int32_t logical = t / block_size;
+  if (t < 0 || logical >= width) return -1;
+  const int32_t blk = row[logical];
+  if (blk < 0 || blk >= num_blocks) return -1;
+  return static_cast<int64_t>(blk) * block_size + t % block_size;
+}
+
+}  // namespace
+
+extern "C" const char* nv_status_string(nv_status status) {
+  switch (status) {
+    case NV_OK: return "ok";
+    case NV_ERR_INVALID_ARG: return "invalid argument";
+    case NV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case NV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t batch,
+                                       int32_t block_size, int32_t num_blocks,
+                                       int32_t* slot_mapping, int32_t* max_context_len) {
+  if (batch < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      !max_context_len)
+    return NV_ERR_INVALID_ARG;
+  if (batch > 0 && (!block_tables || !context_lens || !slot_mapping)) return NV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return NV_ERR_UNSUPPORTED;
+  int32_t mx = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t L = context_lens[b];
+    if (L < 1) return NV_ERR_INVALID_ARG;
+    const int64_t slot = slot_for(block_tables + static_cast<int64_t>(b) * max_blocks_per_seq,
+                                  max_blocks_per_seq, L - 1, block_size, num_blocks);
+    if (slot < 0) return NV_ERR_INVALID_ARG;
+    slot_mapping[b] = static_cast<int32_t>(slot);
+    if (L > mx) mx = L;
+  }
+  *max_context_len = mx;
+  return NV_OK;
+}
+
+extern "C" nv_status nv_prepare_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* num_cached, const int32_t* num_new,
+                                        int32_t num_seqs, int32_t block_size, int32_t num_blocks,
+                                        int32_t pad_to, int32_t* cu_seqlens_q,
+                                        int32_t* cu_seqlens_k, int32_t* max_seqlen_q,
+                                        int32_t* max_seqlen_k, int32_t* slot_mapping,
+                                        int32_t slot_capacity, int32_t* num_slots) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      pad_to < 1 || slot_capacity < 0)
+    return NV_ERR_INVALID_ARG;
+  if (!cu_seqlens_q || !cu_seqlens_k || !max_seqlen_q || !max_seqlen_k || !num_slots)
+    return NV_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!block_tables || !num_cached || !num_new)) return NV_ERR_INVALID_ARG;
+  if (slot_capacity > 0 && !slot_mapping) return NV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX) return NV_ERR_UNSUPPORTED;
+  int64_t cq = 0, ck = 0, n = 0;
+  int32_t mq = 0, mk = 0;
+  cu_seqlens_q[0] = 0;
+  cu_seqlens_k[0] = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t p = num_cached[s], nn = num_new[s];
+    if (p < 0 || nn < 0) return NV_ERR_INVALID_ARG;
+    const int32_t* row = block_tables + static_cast<int64_t>(s) * max_blocks_per_seq;
+    for (int32_t t = p; t < p + nn; ++t) {
+      const int64_t slot = slot_for(row, max_blocks_per_seq, t, block_size, num_blocks);
+      if (slot < 0) return NV_ERR_INVALID_ARG;
+      if (n >= slot_capacity) return NV_ERR_INVALID_ARG;
+      slot_mapping[n++] = static_cast<int32_t>(slot);
+    }
+    cq += nn;
+    ck += static_cast<int64_t>(p) + nn;
+    if (cq > INT32_MAX || ck > INT32_MAX) return NV_ERR_INVALID_ARG;
+    cu_seqlens_q[s + 1] = static_cast<int32_t>(cq);
+    cu_seqlens_k[s + 1] = static_cast<int32_t>(ck);
+    if (nn > mq) mq = nn;
+    if (p + nn > mk) mk = p + nn;
+  }
+  const int64_t padded = (n + pad_to - 1) / pad_to * pad_to;
+  if (padded > slot_capacity) return NV_ERR_INVALID_ARG;
+  for (int64_t i = n; i < padded; ++i) slot_mapping[i] = -1;
+  *max_seqlen_q = mq;
+  *max_seqlen_k = mk;
+  *num_slots = static_cast<int32_t>(padded);
+  return NV_OK;
+}

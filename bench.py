@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache decode step on one MI355X.
+
+Workload (the headline batch-256 decode): 256 sequences with context lengths
+U[100, 1024] at step 0, 16 query / 8 KV heads, head_dim 128, block size 256, bf16,
+30 % of the sequences sharing the same first 1-2 physical (ref-counted) blocks, and
+50 successive decode steps that each append one token per sequence (a new block is
+taken when a token opens one).  One benchmark step = one decode step of that
+sequence: nv_store_kvcache of the 256 new K/V rows, then nv_paged_decode.  Steps
+cycle through the 50 steps.  All inputs (pool, tables, slots, q, new rows) are
+resident in HBM before timing starts; the host builds no metadata in the timed loop.
+
+Prints ONE JSON line.  Extra measurements (other workloads, cold-cache kernel time)
+go into the same line under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=["c3", "copy"], default=None,
+                    help="run one leg only (for profiler runs)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# byte / flop accounting
+# ---------------------------------------------------------------------------
+
+def decode_bytes(step, shape):
+    """Algorithmic bytes of one decode launch: every distinct physical K/V row it must
+    read (shared blocks once) + q + out + lengths + the block-table entries used."""
+    bs, nb = shape.block_size, shape.num_blocks
+    row = shape.num_kv_heads * shape.head_dim * shape.elem_bytes
+    seen = np.zeros(nb * bs, dtype=bool)
+    logical = 0
+    tbl = 0
+    for b, L in enumerate(step.context_lens):
+        L = int(L)
+        nblk = -(-L // bs)
+        blocks = step.block_tables[b, :nblk].astype(np.int64)
+        offs = np.arange(L)
+        seen[blocks[offs // bs] * bs + offs % bs] = True
+        logical += L
+        tbl += nblk
+    B = len(step.context_lens)
+    qo = 2 * B * shape.num_q_heads * shape.head_dim * shape.elem_bytes
+    unique = int(seen.sum())
+    return (2 * unique * row + qo + 4 * B + 4 * tbl), 2 * logical * row
+
+
+def decode_flops(step, shape):
+    return 4.0 * shape.num_q_heads * shape.head_dim * float(np.sum(step.context_lens))
+
+
+# ---------------------------------------------------------------------------
+# GPU legs
+# ---------------------------------------------------------------------------
+
+def time_decode_steps(dev, steps_idx, torch, flush=None):
+    """Run store+decode for each step index; return per-step (store_ms, decode_ms) from
+    HIP events recorded on the stream the kernels are launched on."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in steps_idx]
+    for (a, b, c), t in zip(ev, steps_idx):
+        if flush is not None:
+            flush()
+        a.record(stream)
+        dev.store(t)
+        b.record(stream)
+        dev.decode(t)
+        c.record(stream)
+    torch.cuda.synchronize()
+    return [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev]
+
+
+def headline(args, torch, extra):
+    from workloads import decode_config
+    from paged_kv_cache_319_amd.harness import DeviceDecode
+    case = decode_config("C3")
+    sh = case.shape
+    nsteps = len(case.steps)
+    dev = DeviceDecode(case, poison=True)
+    acct = [decode_bytes(st, sh) for st in case.steps]
+    flops = [decode_flops(st, sh) for st in case.steps]
+    B = case.batch
+
+    # warmup
+    for i in range(args.warmup):
+        dev.store(i % nsteps)
+        dev.decode(i % nsteps)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    order = [(args.warmup + i) % nsteps for i in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    per = time_decode_steps(dev, order, torch)
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    store_ms = np.array([p[0] for p in per])
+    dec_ms = np.array([p[1] for p in per])
+    alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64)
+    log_bytes = np.array([acct[t][1] for t in order], dtype=np.float64)
+    fl = np.array([flops[t] for t in order])
+    dec_gbs = alg_bytes.sum() / (dec_ms.sum() * 1e-3) / 1e9
+    eff_gbs = log_bytes.sum() / (dec_ms.sum() * 1e-3) / 1e9
+    tokens = B * args.steps
+    value = tokens / wall
+    store_bytes = 2 * 2 * B * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * B
+    res = dict(
+        value=value, wall=wall,
+        ms_per_step=wall * 1e3 / args.steps,
+        decode_us_mean=float(dec_ms.mean() * 1e3),
+        decode_us_p10=float(np.percentile(dec_ms, 10) * 1e3),
+        decode_us_p90=float(np.percentile(dec_ms, 90) * 1e3),
+        store_us_mean=float(store_ms.mean() * 1e3),
+        decode_alg_bytes_per_launch=float(alg_bytes.mean()),
+        decode_gbs=dec_gbs, decode_effective_kv_gbs=eff_gbs,
+        decode_tflops=float(fl.sum() / (dec_ms.sum() * 1e-3) / 1e12),
+        kernel_tokens_per_s=float(B / ((store_ms + dec_ms).mean() * 1e-3)),
+        store_gbs=float(store_bytes / (store_ms.mean() * 1e-3) / 1e9),
+    )
+
+    if not args.no_extra:
+        # Cold-cache kernel times: a 1 GiB write between steps evicts L2 and the MALL
+        # (outside the events).
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        cold = time_decode_steps(dev, order[:20], torch, flush=lambda: scratch.fill_(1.0))
+        cold_ms = np.array([c[1] for c in cold])
+        cb = np.array([acct[t][0] for t in order[:20]])
+        extra["c3_decode_cold_us_mean"] = float(cold_ms.mean() * 1e3)
+        extra["c3_decode_cold_gbs"] = float(cb.sum() / (cold_ms.sum() * 1e-3) / 1e9)
+        del scratch
+    del dev
+    torch.cuda.empty_cache()
+    return case, res
+
+
+def extra_decode(name, torch, reps=20):
+    from workloads import decode_config
+    from paged_kv_cache_319_amd.harness import DeviceDecode
+    case = decode_config(name)
+    dev = DeviceDecode(case, poison=True)
+    b, _ = decode_bytes(case.steps[0], case.shape)
+    dev.store(0)
+    for _ in range(3):
+        dev.decode(0)
+    per = time_decode_steps(dev, [0] * reps, torch)
+    dec = np.array([p[1] for p in per])
+    out = {f"{name.lower()}_decode_us": float(np.median(dec) * 1e3),
+           f"{name.lower()}_decode_gbs": float(b / (np.median(dec) * 1e-3) / 1e9)}
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_prefill(torch, reps=20):
+    from workloads import prefill_config
+    from paged_kv_cache_319_amd.harness import DevicePrefill
+    case = prefill_config()
+    try:
+        dev = DevicePrefill(case, poison=True)
+        dev.store()
+        dev.attend()
+    except Exception as e:  # prefill not available: report, do not fail the bench
+        return {"c5_prefill_error": str(e)}
+    sh = case.shape
+    n = case.num_new.astype(np.float64)
+    p = case.num_cached.astype(np.float64)
+    flops = 4.0 * sh.head_dim * sh.num_q_heads * float(np.sum(n * p + n * (n + 1) / 2))
+    stream = torch.cuda.current_stream()
+    evs = []
+    for _ in range(reps):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        dev.store()
+        b.record(stream)
+        dev.attend()
+        c.record(stream)
+        evs.append((a, b, c))
+    torch.cuda.synchronize()
+    st = np.array([a.elapsed_time(b) for a, b, c in evs])
+    at = np.array([b.elapsed_time(c) for a, b, c in evs])
+    rows = int(case.k_new.shape[0])
+    sbytes = 2 * 2 * int(n.sum()) * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * rows
+    out = {"c5_prefill_us": float(np.median(at) * 1e3),
+           "c5_prefill_tflops": float(flops / (np.median(at) * 1e-3) / 1e12),
+           "c5_prefill_mfma_frac": float(flops / (np.median(at) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
+           "c5_store_us": float(np.median(st) * 1e3),
+           "c5_store_gbs": float(sbytes / (np.median(st) * 1e-3) / 1e9)}
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_calibration(torch, reps=5):
+    """A plain 1 GiB device copy: known bytes for scaling the HBM traffic counters."""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(case, budget_s=12.0):
+    import contextlib
+    import oracle
+    from workloads import np_storage_dtype, poison_bits
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
+    except ImportError:  # pragma: no cover
+        limit = contextlib.nullcontext()
+    sh = case.shape
+    with limit:
+        kc = oracle.new_pool(sh.num_blocks, sh.block_size, sh.num_kv_heads, sh.head_dim,
+                             np_storage_dtype(sh.dtype), poison_bits(sh.dtype))
+        vc = kc.copy()
+        f = case.fill
+        oracle.store_kvcache(kc, vc, f.k, f.v,
+                             oracle.fill_slot_mapping(f.block_tables, f.start, f.end,
+                                                      sh.block_size))
+        # time store + decode of the workload's steps in order, sequence by sequence,
+        # until the budget is spent
+        t0 = time.perf_counter()
+        done = 0
+        steps_done = 0
+        for st in case.steps:
+            slots, _ = oracle.decode_slot_mapping(st.block_tables, st.context_lens,
+                                                  sh.block_size)
+            oracle.store_kvcache(kc, vc, st.k_new, st.v_new, slots)
+            for b in range(case.batch):
+                oracle.paged_decode(st.q[b:b + 1], kc, vc, st.block_tables[b:b + 1],
+                                    st.context_lens[b:b + 1], sh.scale)
+                done += 1
+            steps_done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"store + decode of the first {steps_done} of {len(case.steps)} steps "
+                      f"of the batch-256 workload ({done} decoded tokens), numpy float64, "
+                      f"BLAS limited to 1 thread, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build targets one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    import torch
+    from paged_kv_cache_319_amd import load_library
+    load_library()                                    # fails loudly if not built
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(3)
+    if args.only == "copy":
+        print(json.dumps(copy_calibration(torch)), flush=True)
+        return
+    extra = {}
+    print(f"[bench] headline workload: {args.warmup} warmup + {args.steps} timed steps",
+          file=sys.stderr, flush=True)
+    case, res = headline(args, torch, extra)
+    if not args.no_extra and args.only is None:
+        for name in ("C2", "C4"):
+            print(f"[bench] extra decode {name}", file=sys.stderr, flush=True)
+            extra.update(extra_decode(name, torch))
+        print("[bench] extra prefill C5", file=sys.stderr, flush=True)
+        extra.update(extra_prefill(torch))
+    extra.update({k: res[k] for k in ("decode_us_mean", "decode_us_p10", "decode_us_p90",
+                                      "store_us_mean", "store_gbs", "decode_effective_kv_gbs",
+                                      "decode_tflops", "kernel_tokens_per_s",
+                                      "decode_alg_bytes_per_launch")})
+    cpu = None
+    if not args.no_cpu and args.only is None:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case)
+    sh = case.shape
+    line = {
+        "metric": "paged-decode KV-read GB/s + decode tokens/s at batch 256; % of HBM peak",
+        "value": res["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1)*0.5 q/k/v, random block placement)",
+        "config": {"workload": "batch-256 paged decode with 30% shared prefix blocks, "
+                               "50 successive steps (store + decode per step)",
+                   "batch": case.batch, "q_heads": sh.num_q_heads, "kv_heads": sh.num_kv_heads,
+                   "head_dim": sh.head_dim, "block_size": sh.block_size,
+                   "num_blocks": sh.num_blocks, "context_len": "U[100,1024] + step",
+                   "parallelism": "single GPU"},
+        "decode_kv_read_gbs": res["decode_gbs"],
+        "pct_hbm_peak": res["decode_gbs"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": res["decode_gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": res["decode_gbs"] / HBM_PEAK_GBS,
+                     "traffic": None, "kernel": "paged_decode_kernel<BF16,128,2,4>"},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

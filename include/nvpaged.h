@@ -96,11 +96,11 @@ nv_status nv_store_kvcache(const void* k, const void* v,
  *   context_lens: int32 [batch], each in [1, max_blocks_per_seq * block_size]
  *     and <= max_context_len (a host-side bound used to size the split work).
  *   Accumulation is fp32; the output is rounded to the dtype (nearest-even).
- *   workspace: device memory of at least nv_paged_decode_workspace_size(...)
- *     bytes (may be NULL when that size is 0).  Its leading counter words must
- *     be zero before the first call that uses the buffer (allocate it zeroed);
- *     every completed call leaves them zero again.  Calls that share one
- *     workspace must be ordered on one stream.
+ *   workspace: device scratch of at least nv_paged_decode_workspace_size(...)
+ *     bytes (may be NULL when that size is 0) for the fp32 partial results of
+ *     long sequences, which are split into 256-token chunks and merged by a
+ *     second kernel on the same stream.  No initial contents are required.
+ *     Calls that share one workspace must be ordered on one stream.
  *   out must not alias q, the caches or the workspace.  batch == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 size_t nv_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,

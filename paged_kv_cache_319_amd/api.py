@@ -104,15 +104,14 @@ _ws_cache = {}
 
 
 def decode_workspace(device, nbytes: int) -> Optional[torch.Tensor]:
-    """A zero-initialised workspace of at least nbytes, cached per device.  The decode
-    kernels return its counter words to zero, so the buffer is reusable by later calls
-    ordered on the same stream."""
+    """A decode workspace of at least nbytes, cached per device and reused by later
+    calls (which must be ordered on one stream)."""
     if nbytes == 0:
         return None
     key = torch.device(device)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(nbytes, dtype=torch.uint8, device=key)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=key)
         _ws_cache[key] = buf
     return buf
 

@@ -24,10 +24,10 @@
 //
 // Split merge.  A chunk that covers a whole sequence writes the normalised
 // output directly.  Otherwise every chunk writes (m, l, o) partials to the
-// workspace and bumps a per-(sequence, KV head) counter; the workgroup that
-// arrives last merges the partials (log-sum-exp rescaling) and resets the
-// counter to zero, so one launch does the whole step and the counters are
-// ready for the next call.
+// workspace and a second, small kernel merges them with log-sum-exp
+// rescaling.  (Merging inside the first kernel would need device-scope release
+// and acquire fences per workgroup; on this chip those write back and
+// invalidate a whole L2 and cost far more than the second launch.)
 #include "common.h"
 
 namespace {
@@ -46,7 +46,6 @@ struct DecodeArgs {
   const int32_t* context_lens;
   float* ws_o;
   float* ws_ml;
-  uint32_t* ws_cnt;
   int32_t max_blocks;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -69,7 +68,6 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   __shared__ float sm_sum[NW][G];
   __shared__ __attribute__((aligned(16))) float sm_p[NW][G][kWave];
   __shared__ float sm_o[NW][G][D];
-  __shared__ int sm_last;
 
   const int j = blockIdx.x;
   const int b = blockIdx.y;
@@ -216,7 +214,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
     return;
   }
 
-  // Partials of this chunk.
+  // Partials of this chunk; the merge kernel combines them.
   for (int idx = tid; idx < G * D; idx += 64 * NW) {
     const int h = idx / D, d = idx % D;
     float o = 0.f, l = 0.f;
@@ -232,32 +230,36 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       a.ws_ml[pidx * 2 + 1] = l;
     }
   }
-  __threadfence();
-  __syncthreads();
-  uint32_t* cnt = a.ws_cnt + static_cast<int64_t>(b) * a.num_kv_heads + j;
-  if (tid == 0) sm_last = (atomicAdd(cnt, 1u) == static_cast<uint32_t>(nchunks - 1));
-  __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
+}
 
-  for (int idx = tid; idx < G * D; idx += 64 * NW) {
-    const int h = idx / D, d = idx % D;
-    const int64_t base = (qrow0 + h) * a.max_chunks;
-    float M = -INFINITY;
-    for (int cc = 0; cc < nchunks; ++cc) M = fmaxf(M, a.ws_ml[(base + cc) * 2]);
-    float S = 0.f, O = 0.f;
-    for (int cc = 0; cc < nchunks; ++cc) {
-      const float w = __builtin_amdgcn_exp2f(a.ws_ml[(base + cc) * 2] - M);
-      S = fmaf(w, a.ws_ml[(base + cc) * 2 + 1], S);
-      O = fmaf(w, a.ws_o[(base + cc) * D + d], O);
-    }
-    store_out<DT>(outp + (qrow0 + h) * D + d, O / S);
+// Log-sum-exp merge of the chunk partials of one (sequence, query head):
+//   M = max_c m_c,  out = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c.
+// Sequences that fit in one chunk were finished by the attention kernel.
+template <typename DT, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  using T = typename DT::T;
+  constexpr int CHUNK = kDecodeChunk;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int L = a.context_lens[b];
+  const int nchunks = min((L + CHUNK - 1) / CHUNK, a.max_chunks);
+  if (nchunks <= 1) return;
+  const int d = threadIdx.x;
+  const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_chunks;
+  float M = -INFINITY;
+  for (int cc = 0; cc < nchunks; ++cc) M = fmaxf(M, a.ws_ml[(base + cc) * 2]);
+  float S = 0.f, O = 0.f;
+  for (int cc = 0; cc < nchunks; ++cc) {
+    const float w = __builtin_amdgcn_exp2f(a.ws_ml[(base + cc) * 2] - M);
+    S = fmaf(w, a.ws_ml[(base + cc) * 2 + 1], S);
+    O = fmaf(w, a.ws_o[(base + cc) * D + d], O);
   }
-  if (tid == 0) atomicExch(cnt, 0u);
+  store_out<DT>(static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.num_q_heads + h) * D + d,
+                O / S);
 }
 
 struct WsLayout {
-  size_t cnt_off, ml_off, o_off, total;
+  size_t ml_off, o_off, total;
   int max_chunks;
 };
 
@@ -270,8 +272,7 @@ WsLayout ws_layout(int batch, int hq, int hkv, int d, int max_context_len) {
     w.total = 0;
     return w;
   }
-  w.cnt_off = 0;
-  w.ml_off = round_up(static_cast<size_t>(batch) * hkv * sizeof(uint32_t), 256);
+  w.ml_off = 0;
   w.o_off = w.ml_off + round_up(static_cast<size_t>(batch) * hq * w.max_chunks * 2 * sizeof(float), 256);
   w.total = w.o_off + static_cast<size_t>(batch) * hq * w.max_chunks * d * sizeof(float);
   return w;
@@ -281,6 +282,8 @@ template <typename DT, int D, int G>
 nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.num_kv_heads, batch, a.max_chunks);
   paged_decode_kernel<DT, D, G, kDecodeWaves><<<grid, dim3(64 * kDecodeWaves), 0, s>>>(a);
+  if (a.max_chunks > 1)
+    decode_merge_kernel<DT, D><<<dim3(a.num_q_heads, batch), dim3(D), 0, s>>>(a);
   return nvp_host::launch_status();
 }
 
@@ -342,7 +345,6 @@ extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cac
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   char* ws = static_cast<char*>(workspace);
-  a.ws_cnt = w.total ? reinterpret_cast<uint32_t*>(ws + w.cnt_off) : nullptr;
   a.ws_ml = w.total ? reinterpret_cast<float*>(ws + w.ml_off) : nullptr;
   a.ws_o = w.total ? reinterpret_cast<float*>(ws + w.o_off) : nullptr;
   a.max_blocks = max_blocks_per_seq;

@@ -1,5 +1,408 @@
-// Placeholder until the MFMA prefill kernel lands.
+// Packed varlen causal prefill attention over a paged KV cache, on MFMA.
+//
+// Operation (walkthrough, xingyun3d.csdn.net nano-vllm article, sections 七 and
+// 八): the prefill call takes the packed queries of the uncached tokens, the
+// cache, cu_seqlens_q / cu_seqlens_k and the block table; every key, cached
+// prefix and new token alike, is read from the cache through the block table.
+// Query row i of sequence s is the token at position k_s - n_s + i and, with
+// the causal mask, attends keys 0 .. k_s - n_s + i.  Scores are
+// softmax(Q K^T / sqrt(d)) V ("万字深度解析 Nano-vLLM", section 1.2); query head h
+// reads KV head h / g (same article, section 3.2.1).
+//
+// Tiling.  A workgroup of four waves owns 32 * PB query positions of one
+// sequence and GW query heads that share one KV head (GW * PB = 4): wave w takes
+// head w % GW and positions block w / GW.  K/V are walked in tiles of BN keys;
+// each tile is gathered through the block table once per workgroup into LDS
+// (K row-major, V transposed) and serves all four waves.
+//
+// Per wave and tile, with v_mfma_f32_32x32x16_bf16 (eight v_mfma_f32_32x32x2f32
+// for fp32 data):
+//   S^T[key, query] = K Q^T     -- A = K rows from LDS, B = Q held in registers;
+//   online softmax per query column: the accumulator layout gives each lane one
+//   query and 16 of the keys of a 32-key block, the other 16 sit in lane ^ 32,
+//   so the row maximum costs one cross-lane exchange;
+//   O^T[d, query] += V^T P^T    -- B = P^T straight from the S^T registers,
+//   A = V^T from the transposed LDS tile, with the key order matched to the
+//   order in which the S^T accumulator holds the keys.
+// The contraction index of an MFMA may be permuted freely as long as A and B
+// agree, which is what lets P^T feed the second product without a shuffle.
 #include "common.h"
+
+namespace {
+
+using namespace nvp;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Eight contraction elements of one MFMA operand held by one lane.
+template <typename DT>
+struct Frag;
+template <>
+struct Frag<BF16> {
+  u32x4 v;
+};
+template <>
+struct Frag<F32> {
+  u32x4 v[2];
+};
+
+__device__ __forceinline__ f32x16 mma(const Frag<BF16>& a, const Frag<BF16>& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                 __builtin_bit_cast(bf16x8_t, b.v), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mma(const Frag<F32>& a, const Frag<F32>& b, f32x16 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t ae = a.v[e / 4][e % 4], be = b.v[e / 4][e % 4];
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(ae), __uint_as_float(be), c, 0, 0, 0);
+  }
+  return c;
+}
+
+// Eight contiguous elements (a row slice) from memory into a fragment.
+template <typename DT>
+__device__ __forceinline__ void frag_load(Frag<DT>& f, const typename DT::T* p);
+template <>
+__device__ __forceinline__ void frag_load<BF16>(Frag<BF16>& f, const uint16_t* p) {
+  f.v = *reinterpret_cast<const u32x4*>(p);
+}
+template <>
+__device__ __forceinline__ void frag_load<F32>(Frag<F32>& f, const float* p) {
+  f.v[0] = *reinterpret_cast<const u32x4*>(p);
+  f.v[1] = *reinterpret_cast<const u32x4*>(p + 4);
+}
+
+template <typename DT>
+__device__ __forceinline__ void frag_zero(Frag<DT>& f);
+template <>
+__device__ __forceinline__ void frag_zero<BF16>(Frag<BF16>& f) { f.v = u32x4{0, 0, 0, 0}; }
+template <>
+__device__ __forceinline__ void frag_zero<F32>(Frag<F32>& f) {
+  f.v[0] = u32x4{0, 0, 0, 0};
+  f.v[1] = u32x4{0, 0, 0, 0};
+}
+
+// Two runs of four consecutive elements (p0[0..3], p1[0..3]) into a fragment.
+template <typename DT>
+__device__ __forceinline__ void frag_load_2x4(Frag<DT>& f, const typename DT::T* p0,
+                                              const typename DT::T* p1);
+template <>
+__device__ __forceinline__ void frag_load_2x4<BF16>(Frag<BF16>& f, const uint16_t* p0,
+                                                    const uint16_t* p1) {
+  const uint2 a = *reinterpret_cast<const uint2*>(p0);
+  const uint2 b = *reinterpret_cast<const uint2*>(p1);
+  f.v = u32x4{a.x, a.y, b.x, b.y};
+}
+template <>
+__device__ __forceinline__ void frag_load_2x4<F32>(Frag<F32>& f, const float* p0, const float* p1) {
+  f.v[0] = *reinterpret_cast<const u32x4*>(p0);
+  f.v[1] = *reinterpret_cast<const u32x4*>(p1);
+}
+
+// Softmax weights (fp32) -> fragment of the data type.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+  const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+
+template <typename DT>
+__device__ __forceinline__ void frag_from_f32(Frag<DT>& f, const float* x);
+template <>
+__device__ __forceinline__ void frag_from_f32<BF16>(Frag<BF16>& f, const float* x) {
+  f.v = u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+              pack_bf16(x[6], x[7])};
+}
+template <>
+__device__ __forceinline__ void frag_from_f32<F32>(Frag<F32>& f, const float* x) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e / 4][e % 4] = __float_as_uint(x[e]);
+}
+
+// Four output elements (consecutive head_dim positions) -> memory.
+template <typename DT>
+__device__ __forceinline__ void store4(typename DT::T* p, float a, float b, float c, float d);
+template <>
+__device__ __forceinline__ void store4<BF16>(uint16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16),
+                                            f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16));
+}
+template <>
+__device__ __forceinline__ void store4<F32>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Transpose four 16-byte key-row slices (keys x0..x3, EPC elements each) into EPC
+// runs of four keys and write them to the transposed V tile.
+template <typename DT>
+__device__ __forceinline__ void write_vt(typename DT::T* vt, int vrow, int d0, int k0,
+                                         const u32x4* r);
+template <>
+__device__ __forceinline__ void write_vt<BF16>(uint16_t* vt, int vrow, int d0, int k0,
+                                               const u32x4* r) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    // element 2m (low halves) and 2m + 1 (high halves) of each key
+    const uint32_t lo01 = (r[0][m] & 0xffffu) | (r[1][m] << 16);
+    const uint32_t lo23 = (r[2][m] & 0xffffu) | (r[3][m] << 16);
+    const uint32_t hi01 = (r[0][m] >> 16) | (r[1][m] & 0xffff0000u);
+    const uint32_t hi23 = (r[2][m] >> 16) | (r[3][m] & 0xffff0000u);
+    *reinterpret_cast<uint2*>(vt + (d0 + 2 * m) * vrow + k0) = make_uint2(lo01, lo23);
+    *reinterpret_cast<uint2*>(vt + (d0 + 2 * m + 1) * vrow + k0) = make_uint2(hi01, hi23);
+  }
+}
+template <>
+__device__ __forceinline__ void write_vt<F32>(float* vt, int vrow, int d0, int k0, const u32x4* r) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    *reinterpret_cast<u32x4*>(vt + (d0 + m) * vrow + k0) = u32x4{r[0][m], r[1][m], r[2][m], r[3][m]};
+}
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t group;
+  int32_t causal;
+  float scale_log2;
+};
+
+template <typename DT, int D, int GW, int PB, int BN>
+__global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a) {
+  using T = typename DT::T;
+  constexpr int ES = DT::kBytes;
+  constexpr int EPC = 16 / ES;           // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;           // chunks per key row
+  constexpr int KSTEPS = D / 16;         // contraction steps over head_dim
+  constexpr int DT32 = D / 32;           // 32-row output tiles over head_dim
+  constexpr int NKB = BN / 32;           // 32-key blocks per tile
+  constexpr int NKS = BN / 16;           // 16-key contraction slices per tile
+  constexpr int KROW = D + EPC;          // padded K row (elements)
+  constexpr int VROW = BN + 4;           // padded transposed-V row (elements)
+  constexpr int UNITS = (BN / 4) * CPR;  // 4-key x 16-byte staging units per tile
+  constexpr int UPT = (UNITS + 255) / 256;
+  constexpr int BMW = 32 * PB;           // query positions per workgroup
+  static_assert(GW * PB == 4, "four waves per workgroup");
+
+  __shared__ __attribute__((aligned(16))) T ks[BN * KROW];
+  __shared__ __attribute__((aligned(16))) T vt[D * VROW];
+
+  const int s = blockIdx.z;
+  const int q_begin = a.cu_q[s];
+  const int n = a.cu_q[s + 1] - q_begin;
+  const int qt = gridDim.x - 1 - blockIdx.x;   // heavy (late) tiles are dispatched first
+  const int wg_q0 = qt * BMW;
+  if (wg_q0 >= n) return;                      // uniform over the workgroup
+  const int k_len = a.cu_k[s + 1] - a.cu_k[s];
+  const int p0 = k_len - n;                    // cached prefix length
+
+  const int subgroups = a.group / GW;
+  const int j = blockIdx.y / subgroups;
+  const int sub = blockIdx.y % subgroups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = wave_id();
+  const int head = j * a.group + sub * GW + (wave % GW);
+  const int q0 = wg_q0 + (wave / GW) * 32;     // first query row of this wave
+  const int qi = lane & 31;                    // query column held by this lane
+  const int hh = lane >> 5;                    // contraction half held by this lane
+
+  const int k_end = a.causal ? p0 + min(wg_q0 + BMW, n) : k_len;  // keys any row can see
+  const int ntiles = (k_end + BN - 1) / BN;
+
+  const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
+  const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
+  const int32_t* __restrict__ bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const int64_t slot_stride = static_cast<int64_t>(a.num_kv_heads) * D;
+
+  // Q^T operand: query row q0 + qi, head_dim elements 16*kk + 8*hh + 0..7.
+  Frag<DT> qf[KSTEPS];
+  {
+    const bool qv = q0 + qi < n;
+    const T* qp = static_cast<const T*>(a.q) +
+                  (static_cast<int64_t>(q_begin + q0 + qi) * a.num_q_heads + head) * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (qv) frag_load<DT>(qf[kk], qp + 16 * kk);
+      else frag_zero<DT>(qf[kk]);
+    }
+  }
+
+  // Staging registers for one tile: UPT units of 4 keys x one 16-byte chunk, K and V.
+  u32x4 kst[UPT][4], vst[UPT][4];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + 256 * u;
+      const int c = unit % CPR;
+      const int kg = unit / CPR;
+      const int kp0 = tile * BN + 4 * kg;       // first of the unit's four keys
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kst[u][x] = u32x4{0, 0, 0, 0};
+        vst[u][x] = u32x4{0, 0, 0, 0};
+      }
+      if (unit < UNITS && kp0 < k_end) {
+        const int blk = bt[kp0 / a.block_size];
+        const int64_t slot0 = static_cast<int64_t>(blk) * a.block_size + kp0 % a.block_size;
+        const int64_t e0 = slot0 * slot_stride + static_cast<int64_t>(j) * D + c * EPC;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (kp0 + x < k_end) {
+            kst[u][x] = load16(kc + e0 + x * slot_stride);
+            vst[u][x] = load16(vc + e0 + x * slot_stride);
+          }
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + 256 * u;
+      if (unit < UNITS) {
+        const int c = unit % CPR;
+        const int kg = unit / CPR;
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          *reinterpret_cast<u32x4*>(&ks[(4 * kg + x) * KROW + c * EPC]) = kst[u][x];
+        write_vt<DT>(vt, VROW, c * EPC, 4 * kg, vst[u]);
+      }
+    }
+  };
+
+  f32x16 oacc[DT32];
+#pragma unroll
+  for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -INFINITY;   // running max of this lane's query (log2 domain)
+  float l_run = 0.f;         // running sum over this lane's half of the keys
+
+  const int qpos = p0 + q0 + qi;                        // absolute position of the query
+  const int key_limit = a.causal ? min(qpos + 1, k_len) : k_len;
+
+  load_tile(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();          // every wave is done reading the previous tile
+    store_tile();
+    __syncthreads();
+    if (tile + 1 < ntiles) load_tile(tile + 1);   // in flight while this tile computes
+
+    // S^T = K Q^T for each 32-key block of the tile.
+    f32x16 sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        Frag<DT> kf;
+        frag_load<DT>(kf, &ks[(32 * kb + qi) * KROW + 16 * kk + 8 * hh]);
+        sacc[kb] = mma(kf, qf[kk], sacc[kb]);
+      }
+    }
+
+    // Mask, scale, tile maximum.  Register r of block kb holds key
+    // 32*kb + 8*(r/4) + 4*hh + r%4 of the tile, for query column qi.
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = tile * BN + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+        const float v = key < key_limit ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+        sacc[kb][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    m_run = m_new;
+
+    float psum = 0.f;
+    Frag<DT> pf[NKS];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(sacc[kb][r] - m_ref);
+        psum += p[r];
+      }
+      frag_from_f32<DT>(pf[2 * kb], p);
+      frag_from_f32<DT>(pf[2 * kb + 1], p + 8);
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+    // O^T += V^T P^T.  Fragment element e of slice ks holds key
+    // 16*ks + 8*(e/4) + 4*hh + e%4, matching the S^T register order above.
+#pragma unroll
+    for (int dt = 0; dt < DT32; ++dt) {
+      const T* vrow = &vt[(32 * dt + qi) * VROW];
+#pragma unroll
+      for (int ksl = 0; ksl < NKS; ++ksl) {
+        Frag<DT> vf;
+        frag_load_2x4<DT>(vf, vrow + 16 * ksl + 4 * hh, vrow + 16 * ksl + 8 + 4 * hh);
+        oacc[dt] = mma(vf, pf[ksl], oacc[dt]);
+      }
+    }
+  }
+
+  // Normalise and write.  O^T register r of tile dt is head_dim position
+  // 32*dt + 8*(r/4) + 4*hh + r%4 of query q0 + qi.
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (q0 + qi < n) {
+    const float inv = 1.f / l_tot;
+    T* op = static_cast<T*>(a.out) +
+            (static_cast<int64_t>(q_begin + q0 + qi) * a.num_q_heads + head) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        store4<DT>(op + 32 * dt + 8 * g4 + 4 * hh, oacc[dt][4 * g4] * inv,
+                   oacc[dt][4 * g4 + 1] * inv, oacc[dt][4 * g4 + 2] * inv,
+                   oacc[dt][4 * g4 + 3] * inv);
+  }
+}
+
+template <typename DT, int D, int GW, int PB>
+nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, hipStream_t s) {
+  constexpr int BN = DT::kBytes == 2 ? 64 : 32;
+  const int tiles = (max_seqlen_q + 32 * PB - 1) / (32 * PB);
+  if (tiles <= 0) return NV_OK;
+  dim3 grid(tiles, a.num_kv_heads * (a.group / GW), num_seqs);
+  paged_prefill_kernel<DT, D, GW, PB, BN><<<grid, dim3(256), 0, s>>>(a);
+  return nvp_host::launch_status();
+}
+
+template <typename DT, int D>
+nv_status dispatch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, hipStream_t s) {
+  switch (a.group) {
+    case 1: return launch_prefill<DT, D, 1, 4>(a, num_seqs, max_seqlen_q, s);
+    case 2: return launch_prefill<DT, D, 2, 2>(a, num_seqs, max_seqlen_q, s);
+    case 4:
+    case 8: return launch_prefill<DT, D, 4, 1>(a, num_seqs, max_seqlen_q, s);
+    default: return NV_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
 
 extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* cu_seqlens_q,
@@ -9,5 +412,42 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t num_blocks, int32_t block_size, float softmax_scale,
                                       int32_t causal, int32_t dtype, void* stream) {
-  return NV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
+      block_size <= 0 || max_blocks_per_seq <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return NV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
+  if (dtype != NV_F32 && dtype != NV_BF16) return NV_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return NV_ERR_UNSUPPORTED;
+  if (block_size % 16 != 0) return NV_ERR_UNSUPPORTED;
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return NV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || max_seqlen_q == 0) return NV_OK;
+  if (!out || !q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables)
+    return NV_ERR_INVALID_ARG;
+  if (max_seqlen_q > max_seqlen_k ||
+      static_cast<int64_t>(max_seqlen_k) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return NV_ERR_INVALID_ARG;
+  if (num_seqs > 65535 || static_cast<int64_t>(num_kv_heads) * g > 65535) return NV_ERR_UNSUPPORTED;
+
+  PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.block_size = block_size;
+  a.group = g;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == NV_BF16)
+    return head_dim == 128 ? dispatch_prefill<BF16, 128>(a, num_seqs, max_seqlen_q, s)
+                           : dispatch_prefill<BF16, 64>(a, num_seqs, max_seqlen_q, s);
+  return head_dim == 128 ? dispatch_prefill<F32, 128>(a, num_seqs, max_seqlen_q, s)
+                         : dispatch_prefill<F32, 64>(a, num_seqs, max_seqlen_q, s);
 }

@@ -51,8 +51,14 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t block_size;
   int32_t max_chunks;
+  int32_t bs_shift;  // log2(block_size) when it is a power of two, else -1
   float scale_log2;
 };
+
+// Logical block of token t (the paging article's t / B).
+__device__ __forceinline__ int block_of(int t, const DecodeArgs& a) {
+  return a.bs_shift >= 0 ? (t >> a.bs_shift) : (t / a.block_size);
+}
 
 template <typename DT, int D, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
@@ -72,18 +78,12 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   const int j = blockIdx.x;
   const int b = blockIdx.y;
   const int c = blockIdx.z;
-  const int L = a.context_lens[b];
-  const int chunk_start = c * CHUNK;
-  if (chunk_start >= L) return;  // uniform over the workgroup
-  // A length above the host bound max_context_len breaks the contract; clamping keeps
-  // every workspace access inside the chunks that were launched.
-  const int nchunks = min((L + CHUNK - 1) / CHUNK, a.max_chunks);
-
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = wave_id();
   const int row = lane / LPT;
   const int col = lane % LPT;
+  const int chunk_start = c * CHUNK;
   const int t0 = chunk_start + wave * kWave;
 
   const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
@@ -93,27 +93,37 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   const int64_t slot_stride = static_cast<int64_t>(a.num_kv_heads) * D;
   const int64_t head_off = static_cast<int64_t>(j) * D + col * EPL;
   const int qhead0 = j * G;
+  const int last_entry = a.max_blocks - 1;
 
+  // The length, this wave's block-table entry and q are independent loads: issue
+  // them together.  Table indices are clamped into the row; an entry read for a
+  // token at or past the length is never used.
+  const int L = a.context_lens[b];
+  const bool one_block = a.block_size % kWave == 0;  // the wave's 64 tokens share a block
+  const int blk_wave = bt[min(block_of(t0, a), last_entry)];
   u32x4 qr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qr[h] = load16(qp + (static_cast<int64_t>(b) * a.num_q_heads + qhead0 + h) * D + col * EPL);
+  if (chunk_start >= L) return;  // uniform over the workgroup
+  // A length above the host bound max_context_len breaks the contract; clamping keeps
+  // every workspace access inside the chunks that were launched.
+  const int nchunks = min((L + CHUNK - 1) / CHUNK, a.max_chunks);
 
   // Issue every K and V load of this lane before any arithmetic.
   u32x4 kr[ITERS], vr[ITERS];
 #pragma unroll
   for (int i = 0; i < ITERS; ++i) {
     const int tf = t0 + i * TPL;  // first token of this wave load (wave-uniform)
+    const int lb = block_of(tf, a);
+    const int blk = one_block ? blk_wave : bt[min(lb, last_entry)];
     kr[i] = u32x4{0, 0, 0, 0};
     vr[i] = u32x4{0, 0, 0, 0};
-    if (tf < L) {
-      const int blk = bt[tf / a.block_size];
-      const int64_t slot = static_cast<int64_t>(blk) * a.block_size + (tf % a.block_size) + row;
-      if (tf + row < L) {
-        const int64_t e = slot * slot_stride + head_off;
-        kr[i] = load16_stream(kc + e);
-        vr[i] = load16_stream(vc + e);
-      }
+    if (tf + row < L) {
+      const int64_t slot = static_cast<int64_t>(blk) * a.block_size + (tf - lb * a.block_size) + row;
+      const int64_t e = slot * slot_stride + head_off;
+      kr[i] = load16_stream(kc + e);
+      vr[i] = load16_stream(vc + e);
     }
   }
 
@@ -352,6 +362,7 @@ extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cac
   a.num_kv_heads = num_kv_heads;
   a.block_size = block_size;
   a.max_chunks = w.max_chunks;
+  a.bs_shift = nvp_host::is_pow2(block_size) ? __builtin_ctz(static_cast<unsigned>(block_size)) : -1;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == NV_BF16) {

@@ -74,8 +74,8 @@ def decode_flops(step, shape):
 # ---------------------------------------------------------------------------
 
 def time_decode_steps(dev, steps_idx, torch, flush=None):
-    """Run store+decode for each step index; return per-step (store_ms, decode_ms) from
-    HIP events recorded on the stream the kernels are launched on."""
+    """Store then decode, two launches per step; per-step (store_ms, decode_ms) from HIP
+    events recorded on the stream the kernels are launched on."""
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in steps_idx]
@@ -91,6 +91,22 @@ def time_decode_steps(dev, steps_idx, torch, flush=None):
     return [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev]
 
 
+def time_fused_steps(dev, steps_idx, torch, flush=None):
+    """Fused store + decode (nv_paged_decode_store), one call per step; per-step ms from
+    HIP events on the launch stream."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in steps_idx]
+    for (a, b), t in zip(ev, steps_idx):
+        if flush is not None:
+            flush()
+        a.record(stream)
+        dev.step_fused(t)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def headline(args, torch, extra):
     from workloads import decode_config
     from paged_kv_cache_319_amd.harness import DeviceDecode
@@ -101,54 +117,56 @@ def headline(args, torch, extra):
     acct = [decode_bytes(st, sh) for st in case.steps]
     flops = [decode_flops(st, sh) for st in case.steps]
     B = case.batch
+    row = sh.num_kv_heads * sh.head_dim * sh.elem_bytes
+    store_bytes = 2 * 2 * B * row + 4 * B          # K and V rows read + written, slots
 
     # warmup
     for i in range(args.warmup):
-        dev.store(i % nsteps)
-        dev.decode(i % nsteps)
+        dev.step_fused(i % nsteps)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps
+    # timed region: exactly K steps, each the fused store + decode of one step
     order = [(args.warmup + i) % nsteps for i in range(args.steps)]
-    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    per = time_decode_steps(dev, order, torch)
+    step_ms = np.array(time_fused_steps(dev, order, torch))
     t1 = time.perf_counter()
     wall = t1 - t0
-    store_ms = np.array([p[0] for p in per])
-    dec_ms = np.array([p[1] for p in per])
-    alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64)
+    alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64) + store_bytes
     log_bytes = np.array([acct[t][1] for t in order], dtype=np.float64)
     fl = np.array([flops[t] for t in order])
-    dec_gbs = alg_bytes.sum() / (dec_ms.sum() * 1e-3) / 1e9
-    eff_gbs = log_bytes.sum() / (dec_ms.sum() * 1e-3) / 1e9
-    tokens = B * args.steps
-    value = tokens / wall
-    store_bytes = 2 * 2 * B * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * B
+    gbs = alg_bytes.sum() / (step_ms.sum() * 1e-3) / 1e9
     res = dict(
-        value=value, wall=wall,
+        value=B * args.steps / wall, wall=wall,
         ms_per_step=wall * 1e3 / args.steps,
-        decode_us_mean=float(dec_ms.mean() * 1e3),
-        decode_us_p10=float(np.percentile(dec_ms, 10) * 1e3),
-        decode_us_p90=float(np.percentile(dec_ms, 90) * 1e3),
-        store_us_mean=float(store_ms.mean() * 1e3),
-        decode_alg_bytes_per_launch=float(alg_bytes.mean()),
-        decode_gbs=dec_gbs, decode_effective_kv_gbs=eff_gbs,
-        decode_tflops=float(fl.sum() / (dec_ms.sum() * 1e-3) / 1e12),
-        kernel_tokens_per_s=float(B / ((store_ms + dec_ms).mean() * 1e-3)),
-        store_gbs=float(store_bytes / (store_ms.mean() * 1e-3) / 1e9),
+        kernel_us_mean=float(step_ms.mean() * 1e3),
+        kernel_us_p10=float(np.percentile(step_ms, 10) * 1e3),
+        kernel_us_p90=float(np.percentile(step_ms, 90) * 1e3),
+        alg_bytes_per_launch=float(alg_bytes.mean()),
+        gbs=gbs,
+        effective_kv_gbs=float(log_bytes.sum() / (step_ms.sum() * 1e-3) / 1e9),
+        tflops=float(fl.sum() / (step_ms.sum() * 1e-3) / 1e12),
+        kernel_tokens_per_s=float(B / (step_ms.mean() * 1e-3)),
     )
 
     if not args.no_extra:
+        # The same steps as two launches (nv_store_kvcache, then nv_paged_decode).
+        per = time_decode_steps(dev, order[:50], torch)
+        st_ms = np.array([p[0] for p in per])
+        de_ms = np.array([p[1] for p in per])
+        db = np.array([acct[t][0] for t in order[:50]])
+        extra["c3_separate_store_us"] = float(st_ms.mean() * 1e3)
+        extra["c3_separate_decode_us"] = float(de_ms.mean() * 1e3)
+        extra["c3_separate_decode_gbs"] = float(db.sum() / (de_ms.sum() * 1e-3) / 1e9)
+        extra["c3_separate_store_gbs"] = float(store_bytes / (st_ms.mean() * 1e-3) / 1e9)
         # Cold-cache kernel times: a 1 GiB write between steps evicts L2 and the MALL
         # (outside the events).
         scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        cold = time_decode_steps(dev, order[:20], torch, flush=lambda: scratch.fill_(1.0))
-        cold_ms = np.array([c[1] for c in cold])
-        cb = np.array([acct[t][0] for t in order[:20]])
-        extra["c3_decode_cold_us_mean"] = float(cold_ms.mean() * 1e3)
-        extra["c3_decode_cold_gbs"] = float(cb.sum() / (cold_ms.sum() * 1e-3) / 1e9)
+        cold = np.array(time_fused_steps(dev, order[:20], torch,
+                                         flush=lambda: scratch.fill_(1.0)))
+        cb = np.array([acct[t][0] for t in order[:20]]) + store_bytes
+        extra["c3_fused_cold_us_mean"] = float(cold.mean() * 1e3)
+        extra["c3_fused_cold_gbs"] = float(cb.sum() / (cold.sum() * 1e-3) / 1e9)
         del scratch
     del dev
     torch.cuda.empty_cache()
@@ -292,10 +310,9 @@ def main():
             extra.update(extra_decode(name, torch))
         print("[bench] extra prefill C5", file=sys.stderr, flush=True)
         extra.update(extra_prefill(torch))
-    extra.update({k: res[k] for k in ("decode_us_mean", "decode_us_p10", "decode_us_p90",
-                                      "store_us_mean", "store_gbs", "decode_effective_kv_gbs",
-                                      "decode_tflops", "kernel_tokens_per_s",
-                                      "decode_alg_bytes_per_launch")})
+    extra.update({k: res[k] for k in ("kernel_us_mean", "kernel_us_p10", "kernel_us_p90",
+                                      "effective_kv_gbs", "tflops", "kernel_tokens_per_s",
+                                      "alg_bytes_per_launch")})
     cpu = None
     if not args.no_cpu and args.only is None:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -315,16 +332,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1)*0.5 q/k/v, random block placement)",
         "config": {"workload": "batch-256 paged decode with 30% shared prefix blocks, "
-                               "50 successive steps (store + decode per step)",
+                               "50 successive steps (fused store + decode per step)",
                    "batch": case.batch, "q_heads": sh.num_q_heads, "kv_heads": sh.num_kv_heads,
                    "head_dim": sh.head_dim, "block_size": sh.block_size,
                    "num_blocks": sh.num_blocks, "context_len": "U[100,1024] + step",
                    "parallelism": "single GPU"},
-        "decode_kv_read_gbs": res["decode_gbs"],
-        "pct_hbm_peak": res["decode_gbs"] / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "achieved": res["decode_gbs"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": res["decode_gbs"] / HBM_PEAK_GBS,
-                     "traffic": None, "kernel": "paged_decode_kernel<BF16,128,2,4>"},
+        "decode_kv_read_gbs": res["gbs"],
+        "pct_hbm_peak": res["gbs"] / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": res["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": res["gbs"] / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "kernel": "paged_decode_kernel<BF16,128,2,4,fast,store>"},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -95,11 +95,16 @@ nv_status nv_store_kvcache(const void* k, const void* v,
  *   q, out: [batch, num_q_heads, head_dim] contiguous, dtype elements.
  *   context_lens: int32 [batch], each in [1, max_blocks_per_seq * block_size]
  *     and <= max_context_len (a host-side bound used to size the split work).
+ *   schedule: optional int32 [batch] device permutation of 0..batch-1 giving
+ *     the order in which sequences are started (nv_prepare_decode writes the
+ *     length-descending order); NULL = 0..batch-1.  It changes only the order
+ *     of work, never the result.
  *   Accumulation is fp32; the output is rounded to the dtype (nearest-even).
  *   workspace: device scratch of at least nv_paged_decode_workspace_size(...)
  *     bytes (may be NULL when that size is 0) for the fp32 partial results of
- *     long sequences, which are split into 256-token chunks and merged by a
- *     second kernel on the same stream.  No initial contents are required.
+ *     sequences split into several work items (done when batch * num_kv_heads
+ *     is too small to fill the GPU), merged by a second kernel on the same
+ *     stream.  No initial contents are required.
  *     Calls that share one workspace must be ordered on one stream.
  *   out must not alias q, the caches or the workspace.  batch == 0 is a no-op.
  * ------------------------------------------------------------------------- */
@@ -111,11 +116,37 @@ size_t nv_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
 nv_status nv_paged_decode(void* out, const void* q,
                           const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* context_lens, int32_t max_context_len,
+                          const int32_t* context_lens, const int32_t* schedule,
+                          int32_t max_context_len,
                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t num_blocks, int32_t block_size,
                           float softmax_scale, int32_t dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * fused store + decode: the same result as nv_store_kvcache(k_new, v_new,
+ * k_row_stride, v_row_stride, k_cache, v_cache, slot_mapping, batch, ...)
+ * followed by nv_paged_decode(...) on the same stream, in one launch (plus the
+ * merge launch when sequences are split).  Row b of k_new / v_new is the K/V of
+ * sequence b's decoded token; slot_mapping[b] must be the slot of its position
+ * context_lens[b] - 1 (as nv_prepare_decode writes it) or -1 to skip the store,
+ * in which case that row is read from the cache.  k_new / v_new rows and their
+ * strides must be 16-byte aligned (NV_ERR_UNSUPPORTED otherwise).  Each
+ * workgroup writes the new row of its own KV head and takes that token's K/V
+ * from k_new / v_new, so no read of the written row races the write.
+ * ------------------------------------------------------------------------- */
+nv_status nv_paged_decode_store(void* out, const void* q,
+                                const void* k_new, const void* v_new,
+                                int64_t k_row_stride, int64_t v_row_stride,
+                                const int32_t* slot_mapping,
+                                void* k_cache, void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* schedule,
+                                int32_t max_context_len, int32_t batch,
+                                int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                float softmax_scale, int32_t dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * paged varlen prefill  ([walkthrough] 七: the prefill call takes q, the cache,
@@ -151,11 +182,14 @@ nv_status nv_paged_prefill(void* out, const void* q,
  * ------------------------------------------------------------------------- */
 
 /* Decode: slot_mapping[b] = slot of position context_lens[b] - 1 (the token
- * decoded this step); *max_context_len = max_b context_lens[b] (0 if batch == 0). */
+ * decoded this step); *max_context_len = max_b context_lens[b] (0 if batch == 0).
+ * If schedule is not NULL it receives 0..batch-1 ordered by context length,
+ * longest first (ties in index order), for nv_paged_decode. */
 nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t batch,
                             int32_t block_size, int32_t num_blocks,
-                            int32_t* slot_mapping, int32_t* max_context_len);
+                            int32_t* slot_mapping, int32_t* schedule,
+                            int32_t* max_context_len);
 
 /* Prefill: sequence s has num_cached[s] tokens already in the cache and
  * num_new[s] new tokens at positions num_cached[s] .. num_cached[s]+num_new[s]-1.

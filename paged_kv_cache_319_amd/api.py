@@ -119,12 +119,15 @@ def decode_workspace(device, nbytes: int) -> Optional[torch.Tensor]:
 def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                     v_cache: torch.Tensor, block_tables: torch.Tensor,
                     context_lens: torch.Tensor, max_context_len: int, softmax_scale: float,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    schedule: Optional[torch.Tensor] = None) -> None:
     nb, bs, hkv, d = k_cache.shape
     batch, hq = q.shape[0], q.shape[1]
     dt = _dtype_code(k_cache)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
+    if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
+        raise ValueError("schedule must be int32 with one entry per sequence")
     need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
     if workspace is None:
         workspace = decode_workspace(k_cache.device, need)
@@ -133,9 +136,47 @@ def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     st = _native.load().nv_paged_decode(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_tables, "block_tables"), block_tables.shape[1],
-        _dev(context_lens, "context_lens"), max_context_len, batch, hq, hkv, d, nb, bs,
+        _dev(context_lens, "context_lens"),
+        _dev(schedule, "schedule") if schedule is not None else None,
+        max_context_len, batch, hq, hkv, d, nb, bs,
         float(softmax_scale), dt, ws_ptr, ws_len, _stream(stream, q.device))
     _check("nv_paged_decode", st)
+
+
+def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                          v_new: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, block_tables: torch.Tensor,
+                          context_lens: torch.Tensor, max_context_len: int,
+                          softmax_scale: float, workspace: Optional[torch.Tensor] = None,
+                          stream=None, schedule: Optional[torch.Tensor] = None) -> None:
+    """Store this step's K/V rows and decode, fused into one launch."""
+    nb, bs, hkv, d = k_cache.shape
+    batch, hq = q.shape[0], q.shape[1]
+    dt = _dtype_code(k_cache)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.shape[0] != batch or t.shape[1:] != (hkv, d) or t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name} must be [batch, {hkv}, {d}] with contiguous heads")
+    for name, t in (("block_tables", block_tables), ("context_lens", context_lens),
+                    ("slot_mapping", slot_mapping)):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
+        raise ValueError("schedule must be int32 with one entry per sequence")
+    need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
+    if workspace is None:
+        workspace = decode_workspace(k_cache.device, need)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _native.load().nv_paged_decode_store(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new", False), _dev(v_new, "v_new", False),
+        k_new.stride(0), v_new.stride(0), _dev(slot_mapping, "slot_mapping"),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, "context_lens"),
+        _dev(schedule, "schedule") if schedule is not None else None,
+        max_context_len, batch, hq, hkv, d, nb, bs, float(softmax_scale), dt, ws_ptr, ws_len,
+        _stream(stream, q.device))
+    _check("nv_paged_decode_store", st)
 
 
 # ---------------------------------------------------------------------------
@@ -167,17 +208,23 @@ def nv_paged_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
 # host metadata
 # ---------------------------------------------------------------------------
 
-def nv_prepare_decode(block_tables, context_lens, block_size: int,
-                      num_blocks: int) -> Tuple[np.ndarray, int]:
+def nv_prepare_decode(block_tables, context_lens, block_size: int, num_blocks: int,
+                      with_schedule: bool = False):
+    """Returns (slot_mapping, max_context_len) or, with_schedule, (slot_mapping,
+    schedule, max_context_len); all host arrays."""
     bt = _i32(block_tables)
     cl = _i32(context_lens)
     batch = cl.shape[0]
     slots = np.empty(batch, dtype=np.int32)
+    sched = np.empty(batch, dtype=np.int32) if with_schedule else None
     mx = ctypes.c_int32(0)
     st = _native.load().nv_prepare_decode(_ptr(bt), bt.shape[1] if bt.ndim == 2 else 1,
                                           _ptr(cl), batch, block_size, num_blocks,
-                                          _ptr(slots), ctypes.byref(mx))
+                                          _ptr(slots), _ptr(sched) if with_schedule else None,
+                                          ctypes.byref(mx))
     _check("nv_prepare_decode", st)
+    if with_schedule:
+        return slots, sched, int(mx.value)
     return slots, int(mx.value)
 
 

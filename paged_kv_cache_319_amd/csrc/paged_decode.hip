@@ -1,33 +1,39 @@
-// Paged GQA decode attention with split-K over fixed token chunks.
+// Paged GQA decode attention: length-scheduled work items, online softmax over
+// 256-token passes, split-K with a log-sum-exp merge for long contexts.
 //
 // Operation (walkthrough, xingyun3d.csdn.net nano-vllm article, section 七;
 // softmax(Q K^T / sqrt(d)) V from "万字深度解析 Nano-vLLM", section 1.2): each
 // sequence's single query token attends all context_lens[b] keys of its
-// sequence, fetched through its block table (paging article on gsyq.cn,
-// section 4.1: token t lives in logical block t / B at offset t % B).  Query
-// head h reads KV head h / g ("万字深度解析 Nano-vLLM", section 3.2.1).
+// sequence, fetched through its block table (gsyq.cn paging article, section
+// 4.1: token t lives in logical block t / B at offset t % B).  Query head h
+// reads KV head h / g ("万字深度解析 Nano-vLLM", section 3.2.1).
 //
-// Work decomposition.  One workgroup (NW waves) handles one (KV head j,
-// sequence b, chunk c) triple: tokens [c*CHUNK, (c+1)*CHUNK) of sequence b,
-// CHUNK = 64 * NW.  All g query heads of the group are evaluated against every
-// K/V row the workgroup loads, so each cached byte is read from HBM once.
-// Within a wave a token row of head j (head_dim elements) is spread over LPT
-// lanes holding 16 bytes each, so one wave-wide load instruction fetches TPL
-// whole rows; every lane issues all of its K and V loads up front (64 tokens
-// per wave) to keep many bytes in flight.
+// Work decomposition.  A work item is (KV head j, sequence b, chunk c): tokens
+// [c*chunk, (c+1)*chunk) of sequence b.  The host picks the chunk: whole
+// sequences when batch * kv_heads alone fills the chip, otherwise a length
+// that yields roughly 2048 items.  Sequences are visited in the order of an
+// optional schedule (the host's length-descending order from
+// nv_prepare_decode), so the longest items start first and the short ones fill
+// the tail.  One workgroup of NW waves walks its item in passes of 64*NW
+// tokens; every lane issues all of its K and V loads of a pass (16 + 16
+// non-temporal 16-byte loads) before any arithmetic.
 //
-// Softmax.  Phase 1 forms the scores (v_dot2 for bf16, reductions within the
-// LPT-lane groups by DPP), keeps each token's score in exactly one lane, and
-// takes the chunk maximum across the waves.  Phase 2 exponentiates once per
-// (token, head), publishes the weights through LDS and accumulates P V in fp32.
-// Scores carry a log2(e) factor so the exponentials are exp2.
+// Lanes.  A token row of head j (head_dim elements) is spread over LPT lanes of
+// 16 bytes, so one wave-wide load fetches TPL whole rows.  The g query heads of
+// the group are evaluated against every loaded row: each cached byte is read
+// from HBM once per step.
+//
+// Softmax.  Per pass: scores (v_dot2 for bf16, DPP reductions within LPT-lane
+// groups), each token's score kept in exactly one lane, the pass maximum across
+// waves through LDS, then an online update (running max m, sum l and P V
+// accumulator rescaled by 2^(m_old - m_new)).  Weights reach the P V loop
+// through LDS.  Scores carry a log2(e) factor so the exponentials are exp2.
 //
 // Split merge.  A chunk that covers a whole sequence writes the normalised
-// output directly.  Otherwise every chunk writes (m, l, o) partials to the
-// workspace and a second, small kernel merges them with log-sum-exp
-// rescaling.  (Merging inside the first kernel would need device-scope release
-// and acquire fences per workgroup; on this chip those write back and
-// invalidate a whole L2 and cost far more than the second launch.)
+// output.  Otherwise each chunk writes (m, l, o) partials to the workspace and
+// a second, small kernel merges them.  (Merging inside the first kernel needs
+// device-scope release/acquire fences per workgroup; on this chip each writes
+// back and invalidates a whole L2 and costs far more than the second launch.)
 #include "common.h"
 
 namespace {
@@ -35,7 +41,8 @@ namespace {
 using namespace nvp;
 
 constexpr int kDecodeWaves = 4;
-constexpr int kDecodeChunk = 64 * kDecodeWaves;  // tokens per workgroup
+constexpr int kPass = 64 * kDecodeWaves;  // tokens per workgroup pass
+constexpr int kTargetItems = 2048;        // work items wanted when splitting
 
 struct DecodeArgs {
   void* out;
@@ -44,47 +51,55 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* schedule;  // sequence visiting order, or null for 0..batch-1
+  // Fused store (nv_paged_decode_store): this step's K/V rows and their slots.
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;
+  int64_t k_new_stride;     // elements between rows of k_new / v_new
+  int64_t v_new_stride;
   float* ws_o;
   float* ws_ml;
   int32_t max_blocks;
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t block_size;
+  int32_t chunk;            // tokens per work item, a multiple of kPass
   int32_t max_chunks;
-  int32_t bs_shift;  // log2(block_size) when it is a power of two, else -1
+  int32_t bs_shift;         // log2(block_size) when it is a power of two, else -1
   float scale_log2;
 };
 
-// Logical block of token t (the paging article's t / B).
+// Logical block of token t (the paging article's t / B).  FAST: the block size is a
+// power of two and a multiple of 64, so a wave's 64 tokens never straddle a block.
+template <bool FAST>
 __device__ __forceinline__ int block_of(int t, const DecodeArgs& a) {
-  return a.bs_shift >= 0 ? (t >> a.bs_shift) : (t / a.block_size);
+  return FAST ? (t >> a.bs_shift) : (t / a.block_size);
 }
 
-template <typename DT, int D, int G, int NW>
+template <typename DT, int D, int G, int NW, bool FAST, bool STORE>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   using T = typename DT::T;
   constexpr int EPL = DT::kPerLoad;  // elements per 16-byte lane load
   constexpr int LPT = D / EPL;       // lanes per token row
   constexpr int TPL = kWave / LPT;   // token rows per wave load
-  constexpr int ITERS = LPT;         // loads per lane: 64 tokens per wave
-  constexpr int CHUNK = 64 * NW;
+  constexpr int ITERS = LPT;         // loads per lane per pass: 64 tokens per wave
+  constexpr int PASS = 64 * NW;
   static_assert(ITERS % 4 == 0, "weights are read four at a time");
 
-  __shared__ float sm_max[NW][G];
+  __shared__ float sm_max[2][NW][G];
   __shared__ float sm_sum[NW][G];
   __shared__ __attribute__((aligned(16))) float sm_p[NW][G][kWave];
   __shared__ float sm_o[NW][G][D];
 
   const int j = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = a.schedule ? a.schedule[blockIdx.y] : static_cast<int>(blockIdx.y);
   const int c = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = wave_id();
   const int row = lane / LPT;
   const int col = lane % LPT;
-  const int chunk_start = c * CHUNK;
-  const int t0 = chunk_start + wave * kWave;
 
   const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
   const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
@@ -94,107 +109,141 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   const int64_t head_off = static_cast<int64_t>(j) * D + col * EPL;
   const int qhead0 = j * G;
   const int last_entry = a.max_blocks - 1;
+  const int cs = c * a.chunk;
 
-  // The length, this wave's block-table entry and q are independent loads: issue
+  // The length, the first block-table entry and q are independent loads: issue
   // them together.  Table indices are clamped into the row; an entry read for a
   // token at or past the length is never used.
   const int L = a.context_lens[b];
-  const bool one_block = a.block_size % kWave == 0;  // the wave's 64 tokens share a block
-  const int blk_wave = bt[min(block_of(t0, a), last_entry)];
+  const int slot_new = STORE ? a.new_slots[b] : -1;
+  int blk_wave = bt[min(block_of<FAST>(cs + wave * kWave, a), last_entry)];
   u32x4 qr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h)
     qr[h] = load16(qp + (static_cast<int64_t>(b) * a.num_q_heads + qhead0 + h) * D + col * EPL);
-  if (chunk_start >= L) return;  // uniform over the workgroup
+  if (cs >= L) return;  // uniform over the workgroup
+  const int ce = min(L, cs + a.chunk);
   // A length above the host bound max_context_len breaks the contract; clamping keeps
   // every workspace access inside the chunks that were launched.
-  const int nchunks = min((L + CHUNK - 1) / CHUNK, a.max_chunks);
+  const int nchunks = min((L + a.chunk - 1) / a.chunk, a.max_chunks);
 
-  // Issue every K and V load of this lane before any arithmetic.
-  u32x4 kr[ITERS], vr[ITERS];
+  // Fused store: the K/V row of the decoded token (position L - 1) comes from this
+  // step's input and is written to its cache slot.  Only this workgroup reads that
+  // row of head j, and it reads it from the input, so the write cannot race a read.
+  const T* __restrict__ kn = static_cast<const T*>(a.k_new) + static_cast<int64_t>(b) * a.k_new_stride + head_off;
+  const T* __restrict__ vn = static_cast<const T*>(a.v_new) + static_cast<int64_t>(b) * a.v_new_stride + head_off;
+  const int pos_new = (STORE && slot_new >= 0) ? L - 1 : -1;
+
+  float m_run[G], l_run[G], acc[G][EPL];
 #pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
-    const int tf = t0 + i * TPL;  // first token of this wave load (wave-uniform)
-    const int lb = block_of(tf, a);
-    const int blk = one_block ? blk_wave : bt[min(lb, last_entry)];
-    kr[i] = u32x4{0, 0, 0, 0};
-    vr[i] = u32x4{0, 0, 0, 0};
-    if (tf + row < L) {
-      const int64_t slot = static_cast<int64_t>(blk) * a.block_size + (tf - lb * a.block_size) + row;
-      const int64_t e = slot * slot_stride + head_off;
-      kr[i] = load16_stream(kc + e);
-      vr[i] = load16_stream(vc + e);
-    }
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  // Phase 1: scores.  After the group reduction all LPT lanes of a row hold the
-  // dot product; lane (row, col == i) keeps iteration i's score.
-  float s[G];
+  int par = 0;
+  for (int ps = cs; ps < ce; ps += PASS, par ^= 1) {
+    const int t0 = ps + wave * kWave;
+    if (ps != cs) blk_wave = bt[min(block_of<FAST>(t0, a), last_entry)];
+
+    // Issue every K and V load of this pass before any arithmetic.
+    u32x4 kr[ITERS], vr[ITERS];
 #pragma unroll
-  for (int h = 0; h < G; ++h) s[h] = 0.f;
+    for (int i = 0; i < ITERS; ++i) {
+      const int tf = t0 + i * TPL;  // first token of this wave load (wave-uniform)
+      int blk, off;
+      if constexpr (FAST) {
+        blk = blk_wave;
+        off = tf & (a.block_size - 1);
+      } else {
+        const int lb = block_of<FAST>(tf, a);
+        blk = bt[min(lb, last_entry)];
+        off = tf - lb * a.block_size;
+      }
+      kr[i] = u32x4{0, 0, 0, 0};
+      vr[i] = u32x4{0, 0, 0, 0};
+      if (tf + row < ce) {
+        const int64_t slot = static_cast<int64_t>(blk) * a.block_size + off + row;
+        const int64_t e = slot * slot_stride + head_off;
+        const bool is_new = STORE && tf + row == pos_new;
+        kr[i] = load16_stream(is_new ? kn : kc + e);
+        vr[i] = load16_stream(is_new ? vn : vc + e);
+      }
+    }
+    if (STORE && pos_new >= t0 && pos_new < t0 + kWave && (pos_new - t0) % TPL == row) {
+      const int64_t e = static_cast<int64_t>(slot_new) * slot_stride + head_off;
+      *reinterpret_cast<u32x4*>(const_cast<T*>(kc) + e) = load16(kn);
+      *reinterpret_cast<u32x4*>(const_cast<T*>(vc) + e) = load16(vn);
+    }
+
+    // Scores.  After the group reduction all LPT lanes of a row hold the dot
+    // product; lane (row, col == i) keeps iteration i's score.
+    float s[G];
 #pragma unroll
-  for (int i = 0; i < ITERS; ++i) {
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < ITERS; ++i) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float part = group_sum<LPT>(dot16<DT>(kr[i], qr[h], 0.f));
+        s[h] = (col == i) ? part : s[h];
+      }
+    }
+    const bool valid = (t0 + col * TPL + row) < ce;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float part = group_sum<LPT>(dot16<DT>(kr[i], qr[h], 0.f));
-      s[h] = (col == i) ? part : s[h];
+      s[h] = valid ? s[h] * a.scale_log2 : -INFINITY;
+      const float wm = group_max<kWave>(s[h]);
+      if (lane == 0) sm_max[par][wave][h] = wm;
     }
-  }
-  const bool valid = (t0 + col * TPL + row) < L;
+    __syncthreads();
+
+    // Online update with the workgroup maximum of this pass.
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    s[h] = valid ? s[h] * a.scale_log2 : -INFINITY;
-    const float wm = group_max<kWave>(s[h]);
-    if (lane == 0) sm_max[wave][h] = wm;
-  }
-  __syncthreads();
-  float m[G];
+    for (int h = 0; h < G; ++h) {
+      float x = sm_max[par][0][h];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x = sm_max[0][h];
+      for (int w = 1; w < NW; ++w) x = fmaxf(x, sm_max[par][w][h]);
+      const float m_new = fmaxf(m_run[h], x);  // finite: the first token of a pass is valid
+      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+      m_run[h] = m_new;
+      const float p = valid ? __builtin_amdgcn_exp2f(s[h] - m_new) : 0.f;
+      sm_p[wave][h][lane] = p;
+      l_run[h] = l_run[h] * alpha + p;
 #pragma unroll
-    for (int w = 1; w < NW; ++w) x = fmaxf(x, sm_max[w][h]);
-    m[h] = x;
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+    for (int i = 0; i < ITERS; i += 4) {
+      f32x4 pw[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        pw[h] = *reinterpret_cast<const f32x4*>(&sm_p[wave][h][row * LPT + i]);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float vv[EPL];
+        widen<DT>(vr[i + ii], vv);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw[h][ii], vv[e], acc[h][e]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // sm_p is rewritten by the next pass
   }
 
-  // Phase 2: weights through LDS, then P V.
+  // Fold the TPL rows of each wave, then the waves through LDS.
   float lsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float p = valid ? __builtin_amdgcn_exp2f(s[h] - m[h]) : 0.f;
-    sm_p[wave][h][lane] = p;
-    lsum[h] = group_sum<kWave>(p);
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  float acc[G][EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-
-#pragma unroll
-  for (int i = 0; i < ITERS; i += 4) {
-    f32x4 pw[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      pw[h] = *reinterpret_cast<const f32x4*>(&sm_p[wave][h][row * LPT + i]);
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      float vv[EPL];
-      widen<DT>(vr[i + ii], vv);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pw[h][ii], vv[e], acc[h][e]);
-    }
-  }
-
-  // Fold the TPL rows of the wave, then the waves through LDS.
-#pragma unroll
-  for (int h = 0; h < G; ++h)
+    lsum[h] = group_sum<kWave>(l_run[h]);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = strided_sum<LPT>(acc[h][e]);
+  }
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -209,22 +258,6 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
 
   T* __restrict__ outp = static_cast<T*>(a.out);
   const int64_t qrow0 = static_cast<int64_t>(b) * a.num_q_heads + qhead0;
-
-  if (nchunks == 1) {
-    for (int idx = tid; idx < G * D; idx += 64 * NW) {
-      const int h = idx / D, d = idx % D;
-      float o = 0.f, l = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        o += sm_o[w][h][d];
-        l += sm_sum[w][h];
-      }
-      store_out<DT>(outp + (qrow0 + h) * D + d, o / l);
-    }
-    return;
-  }
-
-  // Partials of this chunk; the merge kernel combines them.
   for (int idx = tid; idx < G * D; idx += 64 * NW) {
     const int h = idx / D, d = idx % D;
     float o = 0.f, l = 0.f;
@@ -233,11 +266,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       o += sm_o[w][h][d];
       l += sm_sum[w][h];
     }
-    const int64_t pidx = (qrow0 + h) * a.max_chunks + c;
-    a.ws_o[pidx * D + d] = o;
-    if (d == 0) {
-      a.ws_ml[pidx * 2] = m[h];
-      a.ws_ml[pidx * 2 + 1] = l;
+    if (nchunks == 1) {
+      store_out<DT>(outp + (qrow0 + h) * D + d, o / l);
+    } else {
+      const int64_t pidx = (qrow0 + h) * a.max_chunks + c;
+      a.ws_o[pidx * D + d] = o;
+      if (d == 0) {
+        a.ws_ml[pidx * 2] = m_run[h];
+        a.ws_ml[pidx * 2 + 1] = l;
+      }
     }
   }
 }
@@ -248,11 +285,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
 template <typename DT, int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   using T = typename DT::T;
-  constexpr int CHUNK = kDecodeChunk;
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int L = a.context_lens[b];
-  const int nchunks = min((L + CHUNK - 1) / CHUNK, a.max_chunks);
+  const int nchunks = min((L + a.chunk - 1) / a.chunk, a.max_chunks);
   if (nchunks <= 1) return;
   const int d = threadIdx.x;
   const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_chunks;
@@ -268,30 +304,46 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
                 O / S);
 }
 
-struct WsLayout {
+// Host-side plan: tokens per work item and the resulting workspace layout.
+struct Plan {
+  int chunk, max_chunks;
   size_t ml_off, o_off, total;
-  int max_chunks;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-WsLayout ws_layout(int batch, int hq, int hkv, int d, int max_context_len) {
-  WsLayout w{};
-  w.max_chunks = max_context_len <= 0 ? 1 : (max_context_len + kDecodeChunk - 1) / kDecodeChunk;
-  if (w.max_chunks <= 1) {
-    w.total = 0;
-    return w;
+Plan make_plan(int batch, int hq, int hkv, int d, int max_context_len) {
+  Plan p{};
+  const int max_len = max_context_len < 1 ? 1 : max_context_len;
+  const int64_t items = static_cast<int64_t>(batch) * hkv;
+  int64_t per_seq = 1;  // chunks per sequence
+  if (items < (kTargetItems * 3) / 4) per_seq = (kTargetItems + items - 1) / items;
+  int64_t chunk = (max_len + per_seq - 1) / per_seq;
+  chunk = static_cast<int64_t>(round_up(static_cast<size_t>(chunk), kPass));
+  p.chunk = static_cast<int>(chunk);
+  p.max_chunks = static_cast<int>((max_len + chunk - 1) / chunk);
+  if (p.max_chunks <= 1) {
+    p.total = 0;
+    return p;
   }
-  w.ml_off = 0;
-  w.o_off = w.ml_off + round_up(static_cast<size_t>(batch) * hq * w.max_chunks * 2 * sizeof(float), 256);
-  w.total = w.o_off + static_cast<size_t>(batch) * hq * w.max_chunks * d * sizeof(float);
-  return w;
+  p.ml_off = 0;
+  p.o_off = round_up(static_cast<size_t>(batch) * hq * p.max_chunks * 2 * sizeof(float), 256);
+  p.total = p.o_off + static_cast<size_t>(batch) * hq * p.max_chunks * d * sizeof(float);
+  return p;
 }
 
 template <typename DT, int D, int G>
 nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.num_kv_heads, batch, a.max_chunks);
-  paged_decode_kernel<DT, D, G, kDecodeWaves><<<grid, dim3(64 * kDecodeWaves), 0, s>>>(a);
+  const dim3 block(64 * kDecodeWaves);
+  const bool fast = a.bs_shift >= 6;
+  if (a.new_slots) {
+    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, true><<<grid, block, 0, s>>>(a);
+    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, true><<<grid, block, 0, s>>>(a);
+  } else {
+    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, false><<<grid, block, 0, s>>>(a);
+    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, false><<<grid, block, 0, s>>>(a);
+  }
   if (a.max_chunks > 1)
     decode_merge_kernel<DT, D><<<dim3(a.num_q_heads, batch), dim3(D), 0, s>>>(a);
   return nvp_host::launch_status();
@@ -317,16 +369,19 @@ extern "C" size_t nv_paged_decode_workspace_size(int32_t batch, int32_t num_q_he
   (void)block_size;
   (void)dtype;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
-  return ws_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len).total;
+  return make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_context_len).total;
 }
 
-extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cache,
-                                     const void* v_cache, const int32_t* block_tables,
-                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                     int32_t max_context_len, int32_t batch, int32_t num_q_heads,
-                                     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
-                                     int32_t block_size, float softmax_scale, int32_t dtype,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+nv_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, const int32_t* schedule,
+                      int32_t max_context_len, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                      int32_t block_size, float softmax_scale, int32_t dtype, void* workspace,
+                      size_t workspace_bytes, void* stream, const void* k_new, const void* v_new,
+                      int64_t k_new_stride, int64_t v_new_stride, const int32_t* new_slots) {
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
       block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
     return NV_ERR_INVALID_ARG;
@@ -339,13 +394,22 @@ extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cac
   if (batch == 0) return NV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return NV_ERR_INVALID_ARG;
+  if (new_slots) {
+    const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+    const int64_t esize = dtype == NV_F32 ? 4 : 2;
+    if (!k_new || !v_new || k_new_stride < row || v_new_stride < row) return NV_ERR_INVALID_ARG;
+    const uintptr_t align = reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                            static_cast<uintptr_t>(k_new_stride * esize) |
+                            static_cast<uintptr_t>(v_new_stride * esize);
+    if (align & 15) return NV_ERR_UNSUPPORTED;  // rows are moved as 16-byte pieces
+  }
   if (max_context_len < 1 ||
       static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return NV_ERR_INVALID_ARG;
   if (batch > 65535) return NV_ERR_UNSUPPORTED;
-  const WsLayout w = ws_layout(batch, num_q_heads, num_kv_heads, head_dim, max_context_len);
-  if (w.max_chunks > 65535) return NV_ERR_UNSUPPORTED;
-  if (w.total > 0 && (!workspace || workspace_bytes < w.total)) return NV_ERR_WORKSPACE_TOO_SMALL;
+  const Plan p = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_context_len);
+  if (p.max_chunks > 65535) return NV_ERR_UNSUPPORTED;
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return NV_ERR_WORKSPACE_TOO_SMALL;
 
   DecodeArgs a{};
   a.out = out;
@@ -354,14 +418,21 @@ extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cac
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.schedule = schedule;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_slots = new_slots;
+  a.k_new_stride = k_new_stride;
+  a.v_new_stride = v_new_stride;
   char* ws = static_cast<char*>(workspace);
-  a.ws_ml = w.total ? reinterpret_cast<float*>(ws + w.ml_off) : nullptr;
-  a.ws_o = w.total ? reinterpret_cast<float*>(ws + w.o_off) : nullptr;
+  a.ws_ml = p.total ? reinterpret_cast<float*>(ws + p.ml_off) : nullptr;
+  a.ws_o = p.total ? reinterpret_cast<float*>(ws + p.o_off) : nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.block_size = block_size;
-  a.max_chunks = w.max_chunks;
+  a.chunk = p.chunk;
+  a.max_chunks = p.max_chunks;
   a.bs_shift = nvp_host::is_pow2(block_size) ? __builtin_ctz(static_cast<unsigned>(block_size)) : -1;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -371,4 +442,39 @@ extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cac
   }
   return head_dim == 128 ? dispatch_group<F32, 128>(a, g, batch, s)
                          : dispatch_group<F32, 64>(a, g, batch, s);
+}
+
+}  // namespace
+
+extern "C" nv_status nv_paged_decode(void* out, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                     const int32_t* schedule, int32_t max_context_len,
+                                     int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                     float softmax_scale, int32_t dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     schedule, max_context_len, batch, num_q_heads, num_kv_heads, head_dim,
+                     num_blocks, block_size, softmax_scale, dtype, workspace, workspace_bytes,
+                     stream, nullptr, nullptr, 0, 0, nullptr);
+}
+
+extern "C" nv_status nv_paged_decode_store(void* out, const void* q, const void* k_new,
+                                           const void* v_new, int64_t k_row_stride,
+                                           int64_t v_row_stride, const int32_t* slot_mapping,
+                                           void* k_cache, void* v_cache,
+                                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t* context_lens, const int32_t* schedule,
+                                           int32_t max_context_len, int32_t batch,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t num_blocks,
+                                           int32_t block_size, float softmax_scale, int32_t dtype,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && !slot_mapping) return NV_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     schedule, max_context_len, batch, num_q_heads, num_kv_heads, head_dim,
+                     num_blocks, block_size, softmax_scale, dtype, workspace, workspace_bytes,
+                     stream, k_new, v_new, k_row_stride, v_row_stride,
+                     batch > 0 ? slot_mapping : nullptr);
 }

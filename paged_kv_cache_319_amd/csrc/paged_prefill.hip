@@ -9,11 +9,15 @@
 // softmax(Q K^T / sqrt(d)) V ("万字深度解析 Nano-vLLM", section 1.2); query head h
 // reads KV head h / g (same article, section 3.2.1).
 //
-// Tiling.  A workgroup of four waves owns 32 * PB query positions of one
-// sequence and GW query heads that share one KV head (GW * PB = 4): wave w takes
-// head w % GW and positions block w / GW.  K/V are walked in tiles of BN keys;
+// Tiling.  A workgroup of eight waves owns 32 * PB query positions of one
+// sequence and GW query heads that share one KV head (GW * PB = 8): wave w takes
+// head w % GW and position block w / GW.  K/V are walked in tiles of BN keys;
 // each tile is gathered through the block table once per workgroup into LDS
-// (K row-major, V transposed) and serves all four waves.
+// (K row-major, V transposed) and serves all eight waves.  Two LDS buffers let
+// the next tile's global loads and LDS writes overlap this tile's MFMA work with
+// one barrier per tile; two waves per SIMD hide each other's softmax and LDS
+// latency.  A wave skips tiles that its causal rows cannot see and masks only
+// the tiles that cross its diagonal.
 //
 // Per wave and tile, with v_mfma_f32_32x32x16_bf16 (eight v_mfma_f32_32x32x2f32
 // for fp32 data):
@@ -178,7 +182,7 @@ struct PrefillArgs {
 };
 
 template <typename DT, int D, int GW, int PB, int BN>
-__global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs a) {
   using T = typename DT::T;
   constexpr int ES = DT::kBytes;
   constexpr int EPC = 16 / ES;           // elements per 16-byte chunk
@@ -190,12 +194,13 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a) {
   constexpr int KROW = D + EPC;          // padded K row (elements)
   constexpr int VROW = BN + 4;           // padded transposed-V row (elements)
   constexpr int UNITS = (BN / 4) * CPR;  // 4-key x 16-byte staging units per tile
-  constexpr int UPT = (UNITS + 255) / 256;
+  constexpr int NT = 64 * GW * PB;       // threads per workgroup
+  constexpr int UPT = (UNITS + NT - 1) / NT;
   constexpr int BMW = 32 * PB;           // query positions per workgroup
-  static_assert(GW * PB == 4, "four waves per workgroup");
 
-  __shared__ __attribute__((aligned(16))) T ks[BN * KROW];
-  __shared__ __attribute__((aligned(16))) T vt[D * VROW];
+  // Two K / V^T tile buffers: the next tile is written while this one is read.
+  __shared__ __attribute__((aligned(16))) T ks[2][BN * KROW];
+  __shared__ __attribute__((aligned(16))) T vt[2][D * VROW];
 
   const int s = blockIdx.z;
   const int q_begin = a.cu_q[s];
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a) {
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + 256 * u;
+      const int unit = tid + NT * u;
       const int c = unit % CPR;
       const int kg = unit / CPR;
       const int kp0 = tile * BN + 4 * kg;       // first of the unit's four keys
@@ -266,17 +271,17 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + 256 * u;
+      const int unit = tid + NT * u;
       if (unit < UNITS) {
         const int c = unit % CPR;
         const int kg = unit / CPR;
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          *reinterpret_cast<u32x4*>(&ks[(4 * kg + x) * KROW + c * EPC]) = kst[u][x];
-        write_vt<DT>(vt, VROW, c * EPC, 4 * kg, vst[u]);
+          *reinterpret_cast<u32x4*>(&ks[buf][(4 * kg + x) * KROW + c * EPC]) = kst[u][x];
+        write_vt<DT>(vt[buf], VROW, c * EPC, 4 * kg, vst[u]);
       }
     }
   };
@@ -291,77 +296,98 @@ __global__ __launch_bounds__(256) void paged_prefill_kernel(PrefillArgs a) {
 
   const int qpos = p0 + q0 + qi;                        // absolute position of the query
   const int key_limit = a.causal ? min(qpos + 1, k_len) : k_len;
+  // Per wave: keys visible to every query row (no mask below this) and to any row.
+  const bool wave_active = q0 < n;
+  const int all_see = a.causal ? min(p0 + q0 + 1, k_len) : k_len;
+  const int any_sees = a.causal ? p0 + min(q0 + 32, n) : k_len;
 
   load_tile(0);
+  store_tile(0);
+  __syncthreads();
   for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();          // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
+    const int buf = tile & 1;
     if (tile + 1 < ntiles) load_tile(tile + 1);   // in flight while this tile computes
+    if (wave_active && tile * BN < any_sees) {
+      const T* kst_lds = ks[buf];
+      const T* vt_lds = vt[buf];
+      // S^T = K Q^T for each 32-key block of the tile.
+      f32x16 sacc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          Frag<DT> kf;
+          frag_load<DT>(kf, &kst_lds[(32 * kb + qi) * KROW + 16 * kk + 8 * hh]);
+          sacc[kb] = mma(kf, qf[kk], sacc[kb]);
+        }
+      }
 
-    // S^T = K Q^T for each 32-key block of the tile.
-    f32x16 sacc[NKB];
+      // Mask (only where some key of the tile is hidden from some row), scale, tile
+      // maximum.  Register r of block kb holds key 32*kb + 8*(r/4) + 4*hh + r%4 of the
+      // tile, for query column qi.
+      float tmax = -INFINITY;
+      if ((tile + 1) * BN > all_see) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int key = tile * BN + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+            const float v = key < key_limit ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+            sacc[kb][r] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        Frag<DT> kf;
-        frag_load<DT>(kf, &ks[(32 * kb + qi) * KROW + 16 * kk + 8 * hh]);
-        sacc[kb] = mma(kf, qf[kk], sacc[kb]);
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float v = sacc[kb][r] * a.scale_log2;
+            sacc[kb][r] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      m_run = m_new;
+
+      float psum = 0.f;
+      Frag<DT> pf[NKS];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(sacc[kb][r] - m_ref);
+          psum += p[r];
+        }
+        frag_from_f32<DT>(pf[2 * kb], p);
+        frag_from_f32<DT>(pf[2 * kb + 1], p + 8);
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+
+      // O^T += V^T P^T.  Fragment element e of slice ks holds key
+      // 16*ks + 8*(e/4) + 4*hh + e%4, matching the S^T register order above.
+#pragma unroll
+      for (int dt = 0; dt < DT32; ++dt) {
+        const T* vrow = &vt_lds[(32 * dt + qi) * VROW];
+#pragma unroll
+        for (int ksl = 0; ksl < NKS; ++ksl) {
+          Frag<DT> vf;
+          frag_load_2x4<DT>(vf, vrow + 16 * ksl + 4 * hh, vrow + 16 * ksl + 8 + 4 * hh);
+          oacc[dt] = mma(vf, pf[ksl], oacc[dt]);
+        }
       }
     }
-
-    // Mask, scale, tile maximum.  Register r of block kb holds key
-    // 32*kb + 8*(r/4) + 4*hh + r%4 of the tile, for query column qi.
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = tile * BN + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-        const float v = key < key_limit ? sacc[kb][r] * a.scale_log2 : -INFINITY;
-        sacc[kb][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    m_run = m_new;
-
-    float psum = 0.f;
-    Frag<DT> pf[NKS];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float p[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(sacc[kb][r] - m_ref);
-        psum += p[r];
-      }
-      frag_from_f32<DT>(pf[2 * kb], p);
-      frag_from_f32<DT>(pf[2 * kb + 1], p + 8);
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-
-    // O^T += V^T P^T.  Fragment element e of slice ks holds key
-    // 16*ks + 8*(e/4) + 4*hh + e%4, matching the S^T register order above.
-#pragma unroll
-    for (int dt = 0; dt < DT32; ++dt) {
-      const T* vrow = &vt[(32 * dt + qi) * VROW];
-#pragma unroll
-      for (int ksl = 0; ksl < NKS; ++ksl) {
-        Frag<DT> vf;
-        frag_load_2x4<DT>(vf, vrow + 16 * ksl + 4 * hh, vrow + 16 * ksl + 8 + 4 * hh);
-        oacc[dt] = mma(vf, pf[ksl], oacc[dt]);
-      }
-    }
+    if (tile + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();          // the next tile is in LDS; nobody reads this buffer any more
   }
 
   // Normalise and write.  O^T register r of tile dt is head_dim position
@@ -387,17 +413,18 @@ nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, h
   const int tiles = (max_seqlen_q + 32 * PB - 1) / (32 * PB);
   if (tiles <= 0) return NV_OK;
   dim3 grid(tiles, a.num_kv_heads * (a.group / GW), num_seqs);
-  paged_prefill_kernel<DT, D, GW, PB, BN><<<grid, dim3(256), 0, s>>>(a);
+  paged_prefill_kernel<DT, D, GW, PB, BN><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
   return nvp_host::launch_status();
 }
 
+// Eight waves per workgroup: the GQA group's heads times query-position blocks.
 template <typename DT, int D>
 nv_status dispatch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, hipStream_t s) {
   switch (a.group) {
-    case 1: return launch_prefill<DT, D, 1, 4>(a, num_seqs, max_seqlen_q, s);
-    case 2: return launch_prefill<DT, D, 2, 2>(a, num_seqs, max_seqlen_q, s);
-    case 4:
-    case 8: return launch_prefill<DT, D, 4, 1>(a, num_seqs, max_seqlen_q, s);
+    case 1: return launch_prefill<DT, D, 1, 8>(a, num_seqs, max_seqlen_q, s);
+    case 2: return launch_prefill<DT, D, 2, 4>(a, num_seqs, max_seqlen_q, s);
+    case 4: return launch_prefill<DT, D, 4, 2>(a, num_seqs, max_seqlen_q, s);
+    case 8: return launch_prefill<DT, D, 8, 1>(a, num_seqs, max_seqlen_q, s);
     default: return NV_ERR_UNSUPPORTED;
   }
 }

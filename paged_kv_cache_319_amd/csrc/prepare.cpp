@@ -10,6 +10,8 @@
 // slot = block_tables[s][t / B] * B + t % B.
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "nvpaged.h"
 
 namespace {
@@ -40,7 +42,8 @@ extern "C" const char* nv_status_string(nv_status status) {
 extern "C" nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t batch,
                                        int32_t block_size, int32_t num_blocks,
-                                       int32_t* slot_mapping, int32_t* max_context_len) {
+                                       int32_t* slot_mapping, int32_t* schedule,
+                                       int32_t* max_context_len) {
   if (batch < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 ||
       !max_context_len)
     return NV_ERR_INVALID_ARG;
@@ -57,6 +60,12 @@ extern "C" nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_
     if (L > mx) mx = L;
   }
   *max_context_len = mx;
+  if (schedule) {
+    // Longest sequences first, so their work items start before the short ones.
+    for (int32_t b = 0; b < batch; ++b) schedule[b] = b;
+    std::stable_sort(schedule, schedule + batch,
+                     [context_lens](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
+  }
   return NV_OK;
 }
 

@@ -10,7 +10,8 @@ import numpy as np
 import torch
 
 from .api import (nv_prepare_decode, nv_prepare_prefill, nv_store_kvcache, nv_paged_decode,
-                  nv_paged_prefill, nv_paged_decode_workspace_size, NV_BF16, NV_F32)
+                  nv_paged_decode_store, nv_paged_prefill, nv_paged_decode_workspace_size,
+                  NV_BF16, NV_F32)
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 NV_DTYPE = {"f32": NV_F32, "bf16": NV_BF16}
@@ -64,7 +65,7 @@ class DeviceDecode:
     """A decode workload resident on the device: pools (fill rows stored) and, per step,
     q / new rows / tables / lengths / slots as device tensors."""
 
-    def __init__(self, case, device="cuda:0", poison: bool = True):
+    def __init__(self, case, device="cuda:0", poison: bool = True, scheduled: bool = True):
         sh = case.shape
         self.case = case
         self.device = torch.device(device)
@@ -73,8 +74,8 @@ class DeviceDecode:
         self.steps = []
         max_len = 0
         for st in case.steps:
-            slots, mx = nv_prepare_decode(st.block_tables, st.context_lens, sh.block_size,
-                                          sh.num_blocks)
+            slots, sched, mx = nv_prepare_decode(st.block_tables, st.context_lens,
+                                                 sh.block_size, sh.num_blocks, with_schedule=True)
             max_len = max(max_len, mx)
             self.steps.append(dict(
                 q=to_device(st.q, sh.dtype, self.device),
@@ -82,7 +83,8 @@ class DeviceDecode:
                 v=to_device(st.v_new, sh.dtype, self.device),
                 tables=i32(st.block_tables, self.device),
                 lens=i32(st.context_lens, self.device),
-                slots=i32(slots, self.device), max_len=mx))
+                slots=i32(slots, self.device),
+                schedule=i32(sched, self.device) if scheduled else None, max_len=mx))
         B = case.batch
         self.out = torch.empty((B, sh.num_q_heads, sh.head_dim), dtype=TORCH_DTYPE[sh.dtype],
                                device=self.device)
@@ -99,12 +101,21 @@ class DeviceDecode:
         out = self.out if out is None else out
         nv_paged_decode(out, s["q"], self.kc, self.vc, s["tables"], s["lens"],
                         s["max_len"] if max_len is None else max_len, self.case.shape.scale,
-                        workspace=self.workspace)
+                        workspace=self.workspace, schedule=s["schedule"])
         return out
 
     def step(self, t: int):
         self.store(t)
         return self.decode(t)
+
+    def step_fused(self, t: int, out=None):
+        """Store + decode of step t through the fused entry point."""
+        s = self.steps[t]
+        out = self.out if out is None else out
+        nv_paged_decode_store(out, s["q"], s["k"], s["v"], s["slots"], self.kc, self.vc,
+                              s["tables"], s["lens"], s["max_len"], self.case.shape.scale,
+                              workspace=self.workspace, schedule=s["schedule"])
+        return out
 
 
 class DevicePrefill:

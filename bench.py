@@ -6,8 +6,8 @@ U[100, 1024] at step 0, 16 query / 8 KV heads, head_dim 128, block size 256, bf1
 30 % of the sequences sharing the same first 1-2 physical (ref-counted) blocks, and
 50 successive decode steps that each append one token per sequence (a new block is
 taken when a token opens one).  One benchmark step = one decode step of that
-sequence: nv_store_kvcache of the 256 new K/V rows, then nv_paged_decode.  Steps
-cycle through the 50 steps.  All inputs (pool, tables, slots, q, new rows) are
+sequence: the store of the 256 new K/V rows and the decode, fused in one
+nv_paged_decode_store launch.  Steps cycle through the 50 steps.  All inputs (pool, tables, slots, schedule, q, new rows) are
 resident in HBM before timing starts; the host builds no metadata in the timed loop.
 
 Prints ONE JSON line.  Extra measurements (other workloads, cold-cache kernel time)
@@ -91,9 +91,10 @@ def time_decode_steps(dev, steps_idx, torch, flush=None):
     return [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev]
 
 
-def time_fused_steps(dev, steps_idx, torch, flush=None):
-    """Fused store + decode (nv_paged_decode_store), one call per step; per-step ms from
-    HIP events on the launch stream."""
+def time_fused_steps(dev, steps_idx, torch, flush=None, graphs=True):
+    """Fused store + decode (nv_paged_decode_store), one launch per step, replayed from the
+    step's captured HIP graph (or called eagerly); per-step ms from HIP events recorded on
+    the stream the graph is launched on."""
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in steps_idx]
@@ -101,7 +102,10 @@ def time_fused_steps(dev, steps_idx, torch, flush=None):
         if flush is not None:
             flush()
         a.record(stream)
-        dev.step_fused(t)
+        if graphs:
+            dev.replay(t)
+        else:
+            dev.step_fused(t)
         b.record(stream)
     torch.cuda.synchronize()
     return [a.elapsed_time(b) for a, b in ev]
@@ -125,13 +129,20 @@ def headline(args, torch, extra):
         dev.step_fused(i % nsteps)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, each the fused store + decode of one step
+    # Timed region 1 (the value): exactly K steps, each the fused store + decode of one
+    # step, back to back on the stream with no per-step events (an event pair costs
+    # several microseconds of stream time per step).
     order = [(args.warmup + i) % nsteps for i in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_ms = np.array(time_fused_steps(dev, order, torch))
+    for t in order:
+        dev.step_fused(t)
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    # Timed region 2 (the roofline): the same K steps with a HIP event pair around each
+    # launch on its stream; the kernel's duration per launch.
+    step_ms = np.array(time_fused_steps(dev, order, torch, graphs=False))
     alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64) + store_bytes
     log_bytes = np.array([acct[t][1] for t in order], dtype=np.float64)
     fl = np.array([flops[t] for t in order])
@@ -150,6 +161,10 @@ def headline(args, torch, extra):
     )
 
     if not args.no_extra:
+        # The same fused steps replayed from per-step HIP graphs.
+        dev.capture_graphs()
+        gr = np.array(time_fused_steps(dev, order[:50], torch, graphs=True))
+        extra["c3_fused_graph_replay_us"] = float(gr.mean() * 1e3)
         # The same steps as two launches (nv_store_kvcache, then nv_paged_decode).
         per = time_decode_steps(dev, order[:50], torch)
         st_ms = np.array([p[0] for p in per])

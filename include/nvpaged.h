@@ -163,6 +163,11 @@ nv_status nv_paged_decode_store(void* out, const void* q,
  *   cu_seqlens_q/k: int32 [num_seqs + 1], non-decreasing, starting at 0.
  *   max_seqlen_q >= every n_s and max_seqlen_k >= every k_s (host-side bounds
  *   used to size the grid).  Rows of sequences with n_s == 0 are absent.
+ *   tile_schedule: optional int32 [2 * num_tiles] device array of (sequence,
+ *     query tile) pairs, tile = rows [t * R, (t + 1) * R) with R from
+ *     nv_paged_prefill_tile_rows, listing every non-empty tile exactly once;
+ *     nv_prepare_prefill writes it heaviest first.  NULL = a dense grid over
+ *     max_seqlen_q.  It changes only the order of work, never the result.
  *   out must not alias q or the caches.  num_seqs == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 nv_status nv_paged_prefill(void* out, const void* q,
@@ -170,10 +175,16 @@ nv_status nv_paged_prefill(void* out, const void* q,
                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                            int32_t max_seqlen_q, int32_t max_seqlen_k,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t num_seqs,
+                           const int32_t* tile_schedule, int32_t num_tiles,
+                           int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t num_blocks, int32_t block_size,
                            float softmax_scale, int32_t causal, int32_t dtype,
                            void* stream);
+
+/* Query rows per prefill work tile for this head configuration (0 if unsupported).
+ * A tile schedule for nv_paged_prefill is built with this many rows per tile. */
+int32_t nv_paged_prefill_tile_rows(int32_t num_q_heads, int32_t num_kv_heads);
 
 /* ------------------------------------------------------------------------- *
  * Host-side metadata builders ([walkthrough] 七: prepare_decode /
@@ -196,7 +207,11 @@ nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_blocks_per_
  * Writes cu_seqlens_q/k ([num_seqs + 1]), the maxima, and the slots of the new
  * tokens in packed order followed by -1 up to the next multiple of pad_to
  * (pad_to >= 1).  slot_capacity is the length of slot_mapping; *num_slots
- * receives the padded count.  Returns NV_ERR_INVALID_ARG if it does not fit. */
+ * receives the padded count.  If tile_schedule is not NULL it receives the
+ * (sequence, tile) pairs of every tile of tile_rows query rows, ordered by
+ * causal key count (num_cached + tile end), largest first, ties in order;
+ * tile_capacity counts pairs and *num_tiles receives their number.  Returns
+ * NV_ERR_INVALID_ARG if something does not fit. */
 nv_status nv_prepare_prefill(const int32_t* block_tables, int32_t max_blocks_per_seq,
                              const int32_t* num_cached, const int32_t* num_new,
                              int32_t num_seqs, int32_t block_size, int32_t num_blocks,
@@ -204,7 +219,9 @@ nv_status nv_prepare_prefill(const int32_t* block_tables, int32_t max_blocks_per
                              int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
                              int32_t* max_seqlen_q, int32_t* max_seqlen_k,
                              int32_t* slot_mapping, int32_t slot_capacity,
-                             int32_t* num_slots);
+                             int32_t* num_slots, int32_t tile_rows,
+                             int32_t* tile_schedule, int32_t tile_capacity,
+                             int32_t* num_tiles);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     NV_OK, NV_F32, NV_BF16, NvError,
     nv_status_string, nv_store_kvcache, nv_paged_decode_workspace_size, nv_paged_decode,
     nv_paged_decode_store,
-    nv_paged_prefill, nv_prepare_decode, nv_prepare_prefill, decode_workspace,
+    nv_paged_prefill, nv_paged_prefill_tile_rows, nv_prepare_decode, nv_prepare_prefill,
+    decode_workspace,
 )
 from ._native import LIB_PATH, load as load_library  # noqa: F401

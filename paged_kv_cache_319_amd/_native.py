@@ -35,16 +35,17 @@ SIGNATURES = {
     "nv_paged_prefill": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
-        ctypes.c_int32, ctypes.c_void_p]),
+        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "nv_paged_prefill_tile_rows": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nv_prepare_decode": (ctypes.c_int, [
         c_i32p, ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         c_i32p, c_i32p, c_i32p]),
     "nv_prepare_prefill": (ctypes.c_int, [
         c_i32p, ctypes.c_int32, c_i32p, c_i32p, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, c_i32p, c_i32p, c_i32p, c_i32p, c_i32p,
-        ctypes.c_int32, c_i32p]),
+        ctypes.c_int32, c_i32p, ctypes.c_int32, c_i32p, ctypes.c_int32, c_i32p]),
 }
 
 _lib = None

@@ -128,8 +128,8 @@ def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError("block_tables and context_lens must be int32")
     if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
         raise ValueError("schedule must be int32 with one entry per sequence")
-    need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
-    if workspace is None:
+    if workspace is None:   # the library checks the size of a caller-provided workspace
+        need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
         workspace = decode_workspace(k_cache.device, need)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -162,8 +162,8 @@ def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tenso
             raise ValueError(f"{name} must be int32")
     if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
         raise ValueError("schedule must be int32 with one entry per sequence")
-    need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
-    if workspace is None:
+    if workspace is None:   # the library checks the size of a caller-provided workspace
+        need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
         workspace = decode_workspace(k_cache.device, need)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -187,7 +187,8 @@ def nv_paged_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                      v_cache: torch.Tensor, cu_seqlens_q: torch.Tensor,
                      cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int,
                      block_tables: torch.Tensor, softmax_scale: float, causal: bool = True,
-                     stream=None) -> None:
+                     stream=None, tile_schedule: Optional[torch.Tensor] = None) -> None:
+    """tile_schedule: optional int32 [num_tiles, 2] (sequence, tile) pairs on the device."""
     nb, bs, hkv, d = k_cache.shape
     hq = q.shape[1]
     num_seqs = cu_seqlens_q.numel() - 1
@@ -195,13 +196,21 @@ def nv_paged_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
                     ("block_tables", block_tables)):
         if t.dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
+    if tile_schedule is not None and tile_schedule.dtype != torch.int32:
+        raise ValueError("tile_schedule must be int32")
+    num_tiles = tile_schedule.numel() // 2 if tile_schedule is not None else 0
     st = _native.load().nv_paged_prefill(
         _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(cu_seqlens_k, "cu_seqlens_k"),
         max_seqlen_q, max_seqlen_k, _dev(block_tables, "block_tables"), block_tables.shape[1],
-        num_seqs, hq, hkv, d, nb, bs, float(softmax_scale), int(bool(causal)),
+        num_seqs, _dev(tile_schedule, "tile_schedule") if tile_schedule is not None else None,
+        num_tiles, hq, hkv, d, nb, bs, float(softmax_scale), int(bool(causal)),
         _dtype_code(k_cache), _stream(stream, q.device))
     _check("nv_paged_prefill", st)
+
+
+def nv_paged_prefill_tile_rows(num_q_heads: int, num_kv_heads: int) -> int:
+    return int(_native.load().nv_paged_prefill_tile_rows(num_q_heads, num_kv_heads))
 
 
 # ---------------------------------------------------------------------------
@@ -229,7 +238,9 @@ def nv_prepare_decode(block_tables, context_lens, block_size: int, num_blocks: i
 
 
 def nv_prepare_prefill(block_tables, num_cached, num_new, block_size: int, num_blocks: int,
-                       pad_to: int = 1):
+                       pad_to: int = 1, tile_rows: int = 0):
+    """Returns (cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, slot_mapping) and,
+    with tile_rows > 0, also the [num_tiles, 2] tile schedule; all host arrays."""
     bt = _i32(block_tables)
     p = _i32(num_cached)
     n = _i32(num_new)
@@ -238,10 +249,16 @@ def nv_prepare_prefill(block_tables, num_cached, num_new, block_size: int, num_b
     cu_q = np.empty(S + 1, dtype=np.int32)
     cu_k = np.empty(S + 1, dtype=np.int32)
     slots = np.empty(max(cap, 1), dtype=np.int32)
-    mq, mk, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+    mq, mk, ns, nt = (ctypes.c_int32(0) for _ in range(4))
+    tcap = int(sum(-(-int(x) // tile_rows) for x in n)) if tile_rows > 0 else 0
+    tiles = np.empty((max(tcap, 1), 2), dtype=np.int32) if tile_rows > 0 else None
     st = _native.load().nv_prepare_prefill(
         _ptr(bt), bt.shape[1] if bt.ndim == 2 else 1, _ptr(p), _ptr(n), S, block_size,
         num_blocks, pad_to, _ptr(cu_q), _ptr(cu_k), ctypes.byref(mq), ctypes.byref(mk),
-        _ptr(slots), cap, ctypes.byref(ns))
+        _ptr(slots), cap, ctypes.byref(ns), tile_rows,
+        _ptr(tiles) if tiles is not None else None, tcap, ctypes.byref(nt))
     _check("nv_prepare_prefill", st)
-    return cu_q, cu_k, int(mq.value), int(mk.value), slots[:ns.value].copy()
+    res = (cu_q, cu_k, int(mq.value), int(mk.value), slots[:ns.value].copy())
+    if tile_rows > 0:
+        return res + (tiles[:nt.value].copy(),)
+    return res

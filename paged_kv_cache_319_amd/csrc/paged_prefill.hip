@@ -172,6 +172,7 @@ struct PrefillArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   const int32_t* block_tables;
+  const int32_t* tile_schedule;  // (sequence, query tile) pairs, heaviest first; or null
   int32_t max_blocks;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -202,18 +203,28 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   __shared__ __attribute__((aligned(16))) T ks[2][BN * KROW];
   __shared__ __attribute__((aligned(16))) T vt[2][D * VROW];
 
-  const int s = blockIdx.z;
+  // Work tile: from the host schedule (grid = heads x tiles, heaviest tiles first), or
+  // the dense grid (tiles x heads x sequences, a sequence's late tiles first).
+  int s, qt, hy;
+  if (a.tile_schedule) {
+    hy = blockIdx.x;
+    s = a.tile_schedule[2 * blockIdx.y];
+    qt = a.tile_schedule[2 * blockIdx.y + 1];
+  } else {
+    hy = blockIdx.y;
+    s = blockIdx.z;
+    qt = gridDim.x - 1 - blockIdx.x;
+  }
   const int q_begin = a.cu_q[s];
   const int n = a.cu_q[s + 1] - q_begin;
-  const int qt = gridDim.x - 1 - blockIdx.x;   // heavy (late) tiles are dispatched first
   const int wg_q0 = qt * BMW;
   if (wg_q0 >= n) return;                      // uniform over the workgroup
   const int k_len = a.cu_k[s + 1] - a.cu_k[s];
   const int p0 = k_len - n;                    // cached prefix length
 
   const int subgroups = a.group / GW;
-  const int j = blockIdx.y / subgroups;
-  const int sub = blockIdx.y % subgroups;
+  const int j = hy / subgroups;
+  const int sub = hy % subgroups;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = wave_id();
@@ -243,9 +254,10 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
     }
   }
 
-  // Staging registers for one tile: UPT units of 4 keys x one 16-byte chunk, K and V.
-  u32x4 kst[UPT][4], vst[UPT][4];
-  auto load_tile = [&](int tile) {
+  // Staging registers: two sets of UPT units (4 keys x one 16-byte chunk, K and V), so
+  // each tile's global loads are issued two tiles before its LDS write.
+  u32x4 kA[UPT][4], vA[UPT][4], kB[UPT][4], vB[UPT][4];
+  auto load_tile = [&](int tile, u32x4 (&kst)[UPT][4], u32x4 (&vst)[UPT][4]) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = tid + NT * u;
@@ -271,7 +283,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const u32x4 (&kst)[UPT][4], const u32x4 (&vst)[UPT][4]) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = tid + NT * u;
@@ -301,23 +313,20 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   const int all_see = a.causal ? min(p0 + q0 + 1, k_len) : k_len;
   const int any_sees = a.causal ? p0 + min(q0 + 32, n) : k_len;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < ntiles) load_tile(tile + 1);   // in flight while this tile computes
+  auto compute_tile = [&](int tile, const T* kst_lds, const T* vt_lds) {
     if (wave_active && tile * BN < any_sees) {
-      const T* kst_lds = ks[buf];
-      const T* vt_lds = vt[buf];
       // S^T = K Q^T for each 32-key block of the tile.
+      // The key blocks' accumulation chains are interleaved so consecutive MFMAs are
+      // independent.
       f32x16 sacc[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
           Frag<DT> kf;
           frag_load<DT>(kf, &kst_lds[(32 * kb + qi) * KROW + 16 * kk + 8 * hh]);
           sacc[kb] = mma(kf, qf[kk], sacc[kb]);
@@ -368,26 +377,47 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
         frag_from_f32<DT>(pf[2 * kb + 1], p + 8);
       }
       l_run = l_run * alpha + psum;
+      // Rescale only when some query's maximum moved (alpha == 1 everywhere otherwise).
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int dt = 0; dt < DT32; ++dt)
+        for (int dt = 0; dt < DT32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
 
       // O^T += V^T P^T.  Fragment element e of slice ks holds key
-      // 16*ks + 8*(e/4) + 4*hh + e%4, matching the S^T register order above.
+      // 16*ks + 8*(e/4) + 4*hh + e%4, matching the S^T register order above.  The
+      // head_dim tiles are the inner loop: their accumulators are independent.
 #pragma unroll
-      for (int dt = 0; dt < DT32; ++dt) {
-        const T* vrow = &vt_lds[(32 * dt + qi) * VROW];
+      for (int ksl = 0; ksl < NKS; ++ksl) {
 #pragma unroll
-        for (int ksl = 0; ksl < NKS; ++ksl) {
+        for (int dt = 0; dt < DT32; ++dt) {
+          const T* vrow = &vt_lds[(32 * dt + qi) * VROW];
           Frag<DT> vf;
           frag_load_2x4<DT>(vf, vrow + 16 * ksl + 4 * hh, vrow + 16 * ksl + 8 + 4 * hh);
           oacc[dt] = mma(vf, pf[ksl], oacc[dt]);
         }
       }
     }
-    if (tile + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();          // the next tile is in LDS; nobody reads this buffer any more
+  };
+
+  // Tile t is computed from LDS buffer t % 2 while tile t + 1 sits in staging registers
+  // (its LDS write follows) and tile t + 2's global loads are in flight.
+  load_tile(0, kA, vA);
+  if (ntiles > 1) load_tile(1, kB, vB);
+  store_tile(0, kA, vA);
+  __syncthreads();
+  if (ntiles > 2) load_tile(2, kA, vA);
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    compute_tile(tile, ks[0], vt[0]);
+    if (tile + 1 < ntiles) store_tile(1, kB, vB);
+    __syncthreads();
+    if (tile + 1 >= ntiles) break;
+    if (tile + 3 < ntiles) load_tile(tile + 3, kB, vB);
+    compute_tile(tile + 1, ks[1], vt[1]);
+    if (tile + 2 < ntiles) store_tile(0, kA, vA);
+    __syncthreads();
+    if (tile + 4 < ntiles) load_tile(tile + 4, kA, vA);
   }
 
   // Normalise and write.  O^T register r of tile dt is head_dim position
@@ -408,39 +438,57 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 }
 
 template <typename DT, int D, int GW, int PB>
-nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, hipStream_t s) {
+nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int num_tiles,
+                         hipStream_t s) {
   constexpr int BN = DT::kBytes == 2 ? 64 : 32;
-  const int tiles = (max_seqlen_q + 32 * PB - 1) / (32 * PB);
-  if (tiles <= 0) return NV_OK;
-  dim3 grid(tiles, a.num_kv_heads * (a.group / GW), num_seqs);
+  const int heads_y = a.num_kv_heads * (a.group / GW);
+  dim3 grid;
+  if (a.tile_schedule) {
+    if (num_tiles <= 0) return NV_OK;
+    grid = dim3(heads_y, num_tiles, 1);
+  } else {
+    const int tiles = (max_seqlen_q + 32 * PB - 1) / (32 * PB);
+    if (tiles <= 0) return NV_OK;
+    grid = dim3(tiles, heads_y, num_seqs);
+  }
   paged_prefill_kernel<DT, D, GW, PB, BN><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
   return nvp_host::launch_status();
 }
 
 // Eight waves per workgroup: the GQA group's heads times query-position blocks.
 template <typename DT, int D>
-nv_status dispatch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, hipStream_t s) {
+nv_status dispatch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int num_tiles,
+                           hipStream_t s) {
   switch (a.group) {
-    case 1: return launch_prefill<DT, D, 1, 8>(a, num_seqs, max_seqlen_q, s);
-    case 2: return launch_prefill<DT, D, 2, 4>(a, num_seqs, max_seqlen_q, s);
-    case 4: return launch_prefill<DT, D, 4, 2>(a, num_seqs, max_seqlen_q, s);
-    case 8: return launch_prefill<DT, D, 8, 1>(a, num_seqs, max_seqlen_q, s);
+    case 1: return launch_prefill<DT, D, 1, 8>(a, num_seqs, max_seqlen_q, num_tiles, s);
+    case 2: return launch_prefill<DT, D, 2, 4>(a, num_seqs, max_seqlen_q, num_tiles, s);
+    case 4: return launch_prefill<DT, D, 4, 2>(a, num_seqs, max_seqlen_q, num_tiles, s);
+    case 8: return launch_prefill<DT, D, 8, 1>(a, num_seqs, max_seqlen_q, num_tiles, s);
     default: return NV_ERR_UNSUPPORTED;
   }
 }
 
 }  // namespace
 
+extern "C" int32_t nv_paged_prefill_tile_rows(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return 0;
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return 0;
+  return 32 * (8 / g);  // eight waves: g heads x (8 / g) blocks of 32 query rows
+}
+
 extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* cu_seqlens_q,
                                       const int32_t* cu_seqlens_k, int32_t max_seqlen_q,
                                       int32_t max_seqlen_k, const int32_t* block_tables,
                                       int32_t max_blocks_per_seq, int32_t num_seqs,
+                                      const int32_t* tile_schedule, int32_t num_tiles,
                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t num_blocks, int32_t block_size, float softmax_scale,
                                       int32_t causal, int32_t dtype, void* stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 ||
-      block_size <= 0 || max_blocks_per_seq <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+      block_size <= 0 || max_blocks_per_seq <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
+      num_tiles < 0)
     return NV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
   if (dtype != NV_F32 && dtype != NV_BF16) return NV_ERR_UNSUPPORTED;
@@ -454,7 +502,8 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
   if (max_seqlen_q > max_seqlen_k ||
       static_cast<int64_t>(max_seqlen_k) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return NV_ERR_INVALID_ARG;
-  if (num_seqs > 65535 || static_cast<int64_t>(num_kv_heads) * g > 65535) return NV_ERR_UNSUPPORTED;
+  if (num_seqs > 65535 || static_cast<int64_t>(num_kv_heads) * g > 65535 || num_tiles > 65535)
+    return NV_ERR_UNSUPPORTED;
 
   PrefillArgs a{};
   a.out = out;
@@ -464,6 +513,7 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
   a.block_tables = block_tables;
+  a.tile_schedule = tile_schedule;
   a.max_blocks = max_blocks_per_seq;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -473,8 +523,8 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == NV_BF16)
-    return head_dim == 128 ? dispatch_prefill<BF16, 128>(a, num_seqs, max_seqlen_q, s)
-                           : dispatch_prefill<BF16, 64>(a, num_seqs, max_seqlen_q, s);
-  return head_dim == 128 ? dispatch_prefill<F32, 128>(a, num_seqs, max_seqlen_q, s)
-                         : dispatch_prefill<F32, 64>(a, num_seqs, max_seqlen_q, s);
+    return head_dim == 128 ? dispatch_prefill<BF16, 128>(a, num_seqs, max_seqlen_q, num_tiles, s)
+                           : dispatch_prefill<BF16, 64>(a, num_seqs, max_seqlen_q, num_tiles, s);
+  return head_dim == 128 ? dispatch_prefill<F32, 128>(a, num_seqs, max_seqlen_q, num_tiles, s)
+                         : dispatch_prefill<F32, 64>(a, num_seqs, max_seqlen_q, num_tiles, s);
 }

@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "nvpaged.h"
 
@@ -75,7 +76,9 @@ extern "C" nv_status nv_prepare_prefill(const int32_t* block_tables, int32_t max
                                         int32_t pad_to, int32_t* cu_seqlens_q,
                                         int32_t* cu_seqlens_k, int32_t* max_seqlen_q,
                                         int32_t* max_seqlen_k, int32_t* slot_mapping,
-                                        int32_t slot_capacity, int32_t* num_slots) {
+                                        int32_t slot_capacity, int32_t* num_slots,
+                                        int32_t tile_rows, int32_t* tile_schedule,
+                                        int32_t tile_capacity, int32_t* num_tiles) {
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0 || num_blocks <= 0 ||
       pad_to < 1 || slot_capacity < 0)
     return NV_ERR_INVALID_ARG;
@@ -112,5 +115,29 @@ extern "C" nv_status nv_prepare_prefill(const int32_t* block_tables, int32_t max
   *max_seqlen_q = mq;
   *max_seqlen_k = mk;
   *num_slots = static_cast<int32_t>(padded);
+  if (tile_schedule) {
+    // Attention work tiles (tile_rows query rows of one sequence), heaviest first: a
+    // tile's causal key count is num_cached + the end of its row range.
+    if (tile_rows <= 0 || !num_tiles) return NV_ERR_INVALID_ARG;
+    struct Tile { int64_t keys; int32_t seq, tile; };
+    std::vector<Tile> tiles;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+      const int32_t nn = num_new[s];
+      for (int32_t t = 0; static_cast<int64_t>(t) * tile_rows < nn; ++t) {
+        const int64_t end = std::min<int64_t>(static_cast<int64_t>(t + 1) * tile_rows, nn);
+        tiles.push_back(Tile{num_cached[s] + end, s, t});
+      }
+    }
+    if (static_cast<int64_t>(tiles.size()) > tile_capacity) return NV_ERR_INVALID_ARG;
+    std::stable_sort(tiles.begin(), tiles.end(),
+                     [](const Tile& x, const Tile& y) { return x.keys > y.keys; });
+    for (size_t i = 0; i < tiles.size(); ++i) {
+      tile_schedule[2 * i] = tiles[i].seq;
+      tile_schedule[2 * i + 1] = tiles[i].tile;
+    }
+    *num_tiles = static_cast<int32_t>(tiles.size());
+  } else if (num_tiles) {
+    *num_tiles = 0;
+  }
   return NV_OK;
 }

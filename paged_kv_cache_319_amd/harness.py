@@ -10,8 +10,8 @@ import numpy as np
 import torch
 
 from .api import (nv_prepare_decode, nv_prepare_prefill, nv_store_kvcache, nv_paged_decode,
-                  nv_paged_decode_store, nv_paged_prefill, nv_paged_decode_workspace_size,
-                  NV_BF16, NV_F32)
+                  nv_paged_decode_store, nv_paged_prefill, nv_paged_prefill_tile_rows,
+                  nv_paged_decode_workspace_size, NV_BF16, NV_F32)
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 NV_DTYPE = {"f32": NV_F32, "bf16": NV_BF16}
@@ -117,18 +117,37 @@ class DeviceDecode:
                               workspace=self.workspace, schedule=s["schedule"])
         return out
 
+    def capture_graphs(self, steps=None):
+        """Capture one HIP graph per step holding the fused store + decode launch(es).
+        All buffers are pre-allocated, so the graphs record kernel nodes only."""
+        steps = range(len(self.steps)) if steps is None else steps
+        self.graphs = {}
+        for t in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step_fused(t)
+            self.graphs[t] = g
+        torch.cuda.synchronize()
+        return self.graphs
+
+    def replay(self, t: int):
+        self.graphs[t].replay()
+        return self.out
+
 
 class DevicePrefill:
-    def __init__(self, case, device="cuda:0", poison: bool = True):
+    def __init__(self, case, device="cuda:0", poison: bool = True, scheduled: bool = True):
         sh = case.shape
         self.case = case
         self.device = torch.device(device)
         self.kc, self.vc = new_pools(sh, self.device, poison)
         store_fill(sh, case.fill, self.kc, self.vc)
-        cu_q, cu_k, mq, mk, slots = nv_prepare_prefill(case.block_tables, case.num_cached,
-                                                       case.num_new, sh.block_size,
-                                                       sh.num_blocks, case.pad_to)
+        rows = nv_paged_prefill_tile_rows(sh.num_q_heads, sh.num_kv_heads)
+        cu_q, cu_k, mq, mk, slots, tiles = nv_prepare_prefill(
+            case.block_tables, case.num_cached, case.num_new, sh.block_size, sh.num_blocks,
+            case.pad_to, tile_rows=rows)
         self.meta = (cu_q, cu_k, mq, mk, slots)
+        self.tiles = i32(tiles, self.device) if scheduled and len(tiles) else None
         self.cu_q, self.cu_k = i32(cu_q, self.device), i32(cu_k, self.device)
         self.max_q, self.max_k = mq, mk
         self.slots = i32(slots, self.device)
@@ -144,7 +163,8 @@ class DevicePrefill:
     def attend(self, out=None):
         out = self.out if out is None else out
         nv_paged_prefill(out, self.q, self.kc, self.vc, self.cu_q, self.cu_k, self.max_q,
-                         self.max_k, self.tables, self.case.shape.scale, self.case.causal)
+                         self.max_k, self.tables, self.case.shape.scale, self.case.causal,
+                         tile_schedule=self.tiles)
         return out
 
     def step(self):

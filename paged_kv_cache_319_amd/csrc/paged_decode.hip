@@ -14,12 +14,13 @@
 // that yields roughly 2048 items.  Sequences are visited in the order of an
 // optional schedule (the host's length-descending order from
 // nv_prepare_decode), so the longest items start first and the short ones fill
-// the tail.  One workgroup of NW waves walks its item in passes of 32*NW
-// tokens; every lane issues all of its K and V loads of a pass (8 + 8
-// non-temporal 16-byte loads for bf16, head_dim 128) before any arithmetic.
-// Passes of 32 tokens per wave (rather than 64) keep the kernel at ~112 VGPRs,
-// four waves per SIMD: while one workgroup computes, three others on the CU
-// still have loads in flight (measured 88 us vs 92 us per batch-256 step).
+// the tail.  One workgroup of NW waves walks its item in passes of TPW*NW
+// tokens; every lane issues all of its K and V loads of a pass (4 + 4
+// non-temporal 16-byte loads for bf16, head_dim 128: 16 tokens per wave)
+// before any arithmetic.  Short passes keep the kernel small (~80 VGPRs, six
+// waves per SIMD): while one workgroup computes, the others on the CU still
+// have loads in flight (batch-256 step: 64-token passes 92 us, 32-token 89.6 us,
+// 16-token 87.7 us, event-timed).
 //
 // Lanes.  A token row of head j (head_dim elements) is spread over LPT lanes of
 // 16 bytes, so one wave-wide load fetches TPL whole rows.  The g query heads of
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   constexpr int EPL = DT::kPerLoad;  // elements per 16-byte lane load
   constexpr int LPT = D / EPL;       // lanes per token row
   constexpr int TPL = kWave / LPT;   // token rows per wave load
-  constexpr int ITERS = LPT / 2;     // loads per lane per pass (K and V each)
-  constexpr int TPW = ITERS * TPL;   // tokens per wave per pass: 32
+  constexpr int ITERS = LPT >= 16 ? LPT / 4 : 4;  // loads per lane per pass (K and V each)
+  constexpr int TPW = ITERS * TPL;   // tokens per wave per pass: 16 or 32
   constexpr int PASS = TPW * NW;
-  static_assert(ITERS % 4 == 0 && TPW == 32, "weights are read four at a time");
+  static_assert(ITERS % 4 == 0 && kWave % TPW == 0, "weights are read four at a time");
 
   __shared__ float sm_max[2][NW][G];
   __shared__ float sm_sum[NW][G];

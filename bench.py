@@ -129,35 +129,44 @@ def headline(args, torch, extra):
         dev.step_fused(i % nsteps)
     torch.cuda.synchronize()
 
-    # Timed region 1 (the value): exactly K steps, each the fused store + decode of one
-    # step, back to back on the stream with no per-step events (an event pair costs
-    # several microseconds of stream time per step).
+    # Timed region: exactly K steps, each the fused store + decode of one step, back to
+    # back on the stream.  One HIP event pair on that stream brackets the K launches (an
+    # event pair per launch would add several microseconds of stream time to each), so
+    # event time / K is the kernel's average launch duration; the host clock around the
+    # same region (synchronised on both sides) gives the value.
     order = [(args.warmup + i) % nsteps for i in range(args.steps)]
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for t in order:
         dev.step_fused(t)
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    # Timed region 2 (the roofline): the same K steps with a HIP event pair around each
-    # launch on its stream; the kernel's duration per launch.
-    step_ms = np.array(time_fused_steps(dev, order, torch, graphs=False))
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
     alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64) + store_bytes
     log_bytes = np.array([acct[t][1] for t in order], dtype=np.float64)
     fl = np.array([flops[t] for t in order])
-    gbs = alg_bytes.sum() / (step_ms.sum() * 1e-3) / 1e9
+    span_s = launch_ms * 1e-3 * args.steps
+    gbs = alg_bytes.sum() / span_s / 1e9
+    # Spread of single launches: the same steps with an event pair around each launch
+    # (these durations include the event overhead).
+    step_ms = np.array(time_fused_steps(dev, order, torch, graphs=False))
     res = dict(
         value=B * args.steps / wall, wall=wall,
         ms_per_step=wall * 1e3 / args.steps,
-        kernel_us_mean=float(step_ms.mean() * 1e3),
-        kernel_us_p10=float(np.percentile(step_ms, 10) * 1e3),
-        kernel_us_p90=float(np.percentile(step_ms, 90) * 1e3),
+        kernel_us_mean=launch_ms * 1e3,
+        per_launch_event_us_p10=float(np.percentile(step_ms, 10) * 1e3),
+        per_launch_event_us_p50=float(np.percentile(step_ms, 50) * 1e3),
+        per_launch_event_us_p90=float(np.percentile(step_ms, 90) * 1e3),
         alg_bytes_per_launch=float(alg_bytes.mean()),
         gbs=gbs,
-        effective_kv_gbs=float(log_bytes.sum() / (step_ms.sum() * 1e-3) / 1e9),
-        tflops=float(fl.sum() / (step_ms.sum() * 1e-3) / 1e12),
-        kernel_tokens_per_s=float(B / (step_ms.mean() * 1e-3)),
+        effective_kv_gbs=float(log_bytes.sum() / span_s / 1e9),
+        tflops=float(fl.sum() / span_s / 1e12),
+        kernel_tokens_per_s=float(B / (launch_ms * 1e-3)),
     )
 
     if not args.no_extra:
@@ -174,11 +183,11 @@ def headline(args, torch, extra):
         extra["c3_separate_decode_us"] = float(de_ms.mean() * 1e3)
         extra["c3_separate_decode_gbs"] = float(db.sum() / (de_ms.sum() * 1e-3) / 1e9)
         extra["c3_separate_store_gbs"] = float(store_bytes / (st_ms.mean() * 1e-3) / 1e9)
-        # Cold-cache kernel times: a 1 GiB write between steps evicts L2 and the MALL
-        # (outside the events).
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        cold = np.array(time_fused_steps(dev, order[:20], torch,
-                                         flush=lambda: scratch.fill_(1.0)))
+        # Cold-cache kernel times: reading a 1 GiB buffer between steps (outside the
+        # events) leaves L2 and the 256 MB MALL holding only clean lines of that buffer.
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        cold = np.array(time_fused_steps(dev, order[:20], torch, graphs=False,
+                                         flush=lambda: scratch.sum()))
         cb = np.array([acct[t][0] for t in order[:20]]) + store_bytes
         extra["c3_fused_cold_us_mean"] = float(cold.mean() * 1e3)
         extra["c3_fused_cold_gbs"] = float(cb.sum() / (cold.sum() * 1e-3) / 1e9)
@@ -256,6 +265,46 @@ def copy_calibration(torch, reps=5):
 
 
 # ---------------------------------------------------------------------------
+# HBM traffic recorded by the counter runs
+# ---------------------------------------------------------------------------
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "paged_decode_c3_hbm_traffic.md")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_319_amd", "csrc", f)
+                  for f in ("paged_decode.hip", "common.h")]
+
+
+def decode_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy
+    calibration) from the committed counter summary, or None when that summary was
+    taken on different decode kernel sources than the ones built now."""
+    try:
+        text = open(TRAFFIC_RECORD).read()
+    except OSError:
+        return None
+    rec = {}
+    for line in text.splitlines():
+        if line.startswith("record:"):
+            k, _, v = line[len("record:"):].strip().partition("=")
+            rec[k.strip()] = v.strip()
+    if rec.get("decode_sources_sha256") != decode_source_digest():
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the float64 oracle on a bounded sample of the same workload
 # ---------------------------------------------------------------------------
 
@@ -325,7 +374,8 @@ def main():
             extra.update(extra_decode(name, torch))
         print("[bench] extra prefill C5", file=sys.stderr, flush=True)
         extra.update(extra_prefill(torch))
-    extra.update({k: res[k] for k in ("kernel_us_mean", "kernel_us_p10", "kernel_us_p90",
+    extra.update({k: res[k] for k in ("kernel_us_mean", "per_launch_event_us_p10",
+                                      "per_launch_event_us_p50", "per_launch_event_us_p90",
                                       "effective_kv_gbs", "tflops", "kernel_tokens_per_s",
                                       "alg_bytes_per_launch")})
     cpu = None
@@ -356,7 +406,7 @@ def main():
         "pct_hbm_peak": res["gbs"] / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": res["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["gbs"] / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": recorded_traffic(),
                      "kernel": "paged_decode_kernel<BF16,128,2,4,fast,store>"},
         "cpu_baseline": cpu,
         "extra": extra,

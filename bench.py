@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["c3", "copy"], default=None,
+    ap.add_argument("--only", choices=["c3", "c5", "copy"], default=None,
                     help="run one leg only (for profiler runs)")
     return ap.parse_args()
 
@@ -363,6 +363,9 @@ def main():
         sys.exit(3)
     if args.only == "copy":
         print(json.dumps(copy_calibration(torch)), flush=True)
+        return
+    if args.only == "c5":
+        print(json.dumps(extra_prefill(torch)), flush=True)
         return
     extra = {}
     print(f"[bench] headline workload: {args.warmup} warmup + {args.steps} timed steps",

@@ -392,6 +392,9 @@ nv_status decode_impl(void* out, const void* q, const void* k_cache, const void*
       block_size <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
     return NV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
+      softmax_scale == -INFINITY)
+    return NV_ERR_INVALID_ARG;
   if (dtype != NV_F32 && dtype != NV_BF16) return NV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return NV_ERR_UNSUPPORTED;
   if (block_size % 16 != 0) return NV_ERR_UNSUPPORTED;

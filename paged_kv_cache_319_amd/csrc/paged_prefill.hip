@@ -79,6 +79,18 @@ __device__ __forceinline__ void frag_load<F32>(Frag<F32>& f, const float* p) {
 }
 
 template <typename DT>
+__device__ __forceinline__ void frag_negate(Frag<DT>& f);
+template <>
+__device__ __forceinline__ void frag_negate<BF16>(Frag<BF16>& f) {
+  f.v ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+}
+template <>
+__device__ __forceinline__ void frag_negate<F32>(Frag<F32>& f) {
+  f.v[0] ^= u32x4{0x80000000u, 0x80000000u, 0x80000000u, 0x80000000u};
+  f.v[1] ^= u32x4{0x80000000u, 0x80000000u, 0x80000000u, 0x80000000u};
+}
+
+template <typename DT>
 __device__ __forceinline__ void frag_zero(Frag<DT>& f);
 template <>
 __device__ __forceinline__ void frag_zero<BF16>(Frag<BF16>& f) { f.v = u32x4{0, 0, 0, 0}; }
@@ -105,11 +117,12 @@ __device__ __forceinline__ void frag_load_2x4<F32>(Frag<F32>& f, const float* p0
   f.v[1] = *reinterpret_cast<const u32x4*>(p1);
 }
 
-// Softmax weights (fp32) -> fragment of the data type.
+// Softmax weights (fp32) -> fragment of the data type.  Two values convert in one
+// v_cvt_pk_bf16_f32 (round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
-  const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
-  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <typename DT>
@@ -179,10 +192,12 @@ struct PrefillArgs {
   int32_t block_size;
   int32_t group;
   int32_t causal;
-  float scale_log2;
+  int32_t bs_shift;    // log2(block_size) when it is a power of two, else -1
+  int32_t negate_q;    // the softmax scale is negative: q is negated, scale_log2 > 0
+  float scale_log2;    // |softmax_scale| * log2(e), > 0
 };
 
-template <typename DT, int D, int GW, int PB, int BN>
+template <typename DT, int D, int GW, int PB, int BN, bool POW2>
 __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs a) {
   using T = typename DT::T;
   constexpr int ES = DT::kBytes;
@@ -196,7 +211,8 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   constexpr int VROW = BN + 4;           // padded transposed-V row (elements)
   constexpr int UNITS = (BN / 4) * CPR;  // 4-key x 16-byte staging units per tile
   constexpr int NT = 64 * GW * PB;       // threads per workgroup
-  constexpr int UPT = (UNITS + NT - 1) / NT;
+  constexpr int HALF = NT / 2;           // the first half stages K, the second V
+  constexpr int UPT = (UNITS + HALF - 1) / HALF;
   constexpr int BMW = 32 * PB;           // query positions per workgroup
 
   // Two K / V^T tile buffers: the next tile is written while this one is read.
@@ -241,59 +257,95 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   const int32_t* __restrict__ bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
   const int64_t slot_stride = static_cast<int64_t>(a.num_kv_heads) * D;
 
-  // Q^T operand: query row q0 + qi, head_dim elements 16*kk + 8*hh + 0..7.
+  // Q^T operand: query row q0 + qi, head_dim elements 16*kk + 8*hh + 0..7.  Rows past
+  // the sequence read its first row and are zeroed; the loads complete here, before the
+  // tile loop (the zeroing select consumes them), so no wait inside the loop is left
+  // pending on them.
   Frag<DT> qf[KSTEPS];
   {
     const bool qv = q0 + qi < n;
+    const int qrow = q_begin + (qv ? q0 + qi : 0);
     const T* qp = static_cast<const T*>(a.q) +
-                  (static_cast<int64_t>(q_begin + q0 + qi) * a.num_q_heads + head) * D + 8 * hh;
+                  (static_cast<int64_t>(qrow) * a.num_q_heads + head) * D + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) frag_load<DT>(qf[kk], qp + 16 * kk);
+    // A negative scale is applied as |scale| to -q (a sign flip, exact).
+    const bool neg = a.negate_q != 0;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
-      if (qv) frag_load<DT>(qf[kk], qp + 16 * kk);
-      else frag_zero<DT>(qf[kk]);
+      if (neg) frag_negate<DT>(qf[kk]);
+      if (!qv) frag_zero<DT>(qf[kk]);
     }
   }
 
-  // Staging registers: two sets of UPT units (4 keys x one 16-byte chunk, K and V), so
-  // each tile's global loads are issued two tiles before its LDS write.
-  u32x4 kA[UPT][4], vA[UPT][4], kB[UPT][4], vB[UPT][4];
-  auto load_tile = [&](int tile, u32x4 (&kst)[UPT][4], u32x4 (&vst)[UPT][4]) {
+  // Staging registers: the first half of the workgroup's waves stages K, the second
+  // half V, UPT units (4 keys x one 16-byte chunk) per thread.  Two sets, so each tile's
+  // global loads are issued two tiles before its LDS write.  Every call issues the same
+  // loads (a tile past the end reads the pool's first element), which keeps the
+  // compiler's count of loads in flight exact and its waits minimal.
+  const bool v_role = wave >= (GW * PB) / 2;   // wave-uniform
+  const int rtid = tid - (v_role ? HALF : 0);
+  const T* __restrict__ src = v_role ? vc : kc;
+  u32x4 stA[UPT][4], stB[UPT][4];
+
+  // A 4-key unit never straddles a block (the block size is a multiple of 16).  With a
+  // power-of-two block size the tile's BN keys span at most four blocks whose table
+  // entries are workgroup-uniform (scalar loads, which never wait on the vector loads in
+  // flight); otherwise each unit looks its block up itself.
+  const int last_entry = a.max_blocks - 1;
+  auto load_tile = [&](int tile, u32x4 (&st)[UPT][4]) {
+    int ent[4] = {0, 0, 0, 0};
+    if constexpr (POW2) {
+      const int lb0 = (tile * BN) >> a.bs_shift;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ent[i] = bt[min(lb0 + i, last_entry)];
+    }
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + NT * u;
-      const int c = unit % CPR;
-      const int kg = unit / CPR;
-      const int kp0 = tile * BN + 4 * kg;       // first of the unit's four keys
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        kst[u][x] = u32x4{0, 0, 0, 0};
-        vst[u][x] = u32x4{0, 0, 0, 0};
-      }
-      if (unit < UNITS && kp0 < k_end) {
-        const int blk = bt[kp0 / a.block_size];
-        const int64_t slot0 = static_cast<int64_t>(blk) * a.block_size + kp0 % a.block_size;
-        const int64_t e0 = slot0 * slot_stride + static_cast<int64_t>(j) * D + c * EPC;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          if (kp0 + x < k_end) {
-            kst[u][x] = load16(kc + e0 + x * slot_stride);
-            vst[u][x] = load16(vc + e0 + x * slot_stride);
-          }
+      const int unit = rtid + HALF * u;
+      if (UNITS % HALF == 0 || unit < UNITS) {  // wave-uniform: UNITS is a multiple of 64
+        const int c = unit % CPR;
+        const int kg = unit / CPR;
+        const int kp0 = tile * BN + 4 * kg;     // first of the unit's four keys
+        int blk, off;
+        if constexpr (POW2) {
+          const int i = (4 * kg) >> a.bs_shift;  // 0 when the block holds the whole tile
+          blk = i == 0 ? ent[0] : i == 1 ? ent[1] : i == 2 ? ent[2] : ent[3];
+          off = kp0 & ((1 << a.bs_shift) - 1);
+        } else {
+          const int lb = min(kp0 / a.block_size, last_entry);
+          blk = bt[lb];
+          off = kp0 - lb * a.block_size;
         }
+        const int64_t e0 = (static_cast<int64_t>(blk) * a.block_size + off) * slot_stride +
+                           static_cast<int64_t>(j) * D + c * EPC;
+        // Keys at or past k_end read element 0 of the pool instead; store_tile replaces
+        // them by zero (V must be finite there: its weight is zero).  Deferring that
+        // select keeps these loads in flight until the tile is written to LDS.
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          st[u][x] = load16(src + (kp0 + x < k_end ? e0 + x * slot_stride : 0));
       }
     }
   };
-  auto store_tile = [&](int buf, const u32x4 (&kst)[UPT][4], const u32x4 (&vst)[UPT][4]) {
+  auto store_tile = [&](int buf, int tile, const u32x4 (&st)[UPT][4]) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + NT * u;
-      if (unit < UNITS) {
+      const int unit = rtid + HALF * u;
+      if (UNITS % HALF == 0 || unit < UNITS) {
         const int c = unit % CPR;
         const int kg = unit / CPR;
+        const int kp0 = tile * BN + 4 * kg;
+        u32x4 x4[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          *reinterpret_cast<u32x4*>(&ks[buf][(4 * kg + x) * KROW + c * EPC]) = kst[u][x];
-        write_vt<DT>(vt[buf], VROW, c * EPC, 4 * kg, vst[u]);
+        for (int x = 0; x < 4; ++x) x4[x] = kp0 + x < k_end ? st[u][x] : u32x4{0, 0, 0, 0};
+        if (!v_role) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            *reinterpret_cast<u32x4*>(&ks[buf][(4 * kg + x) * KROW + c * EPC]) = x4[x];
+        } else {
+          write_vt<DT>(vt[buf], VROW, c * EPC, 4 * kg, x4);
+        }
       }
     }
   };
@@ -333,9 +385,10 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
         }
       }
 
-      // Mask (only where some key of the tile is hidden from some row), scale, tile
-      // maximum.  Register r of block kb holds key 32*kb + 8*(r/4) + 4*hh + r%4 of the
-      // tile, for query column qi.
+      // Mask (only where some key of the tile is hidden from some row) and tile maximum
+      // of the raw scores.  Register r of block kb holds key 32*kb + 8*(r/4) + 4*hh + r%4
+      // of the tile, for query column qi.  The scale (> 0) is applied inside the
+      // exponent: 2^(s*scale_log2 - m) with one fma per score.
       float tmax = -INFINITY;
       if ((tile + 1) * BN > all_see) {
 #pragma unroll
@@ -343,7 +396,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = tile * BN + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-            const float v = key < key_limit ? sacc[kb][r] * a.scale_log2 : -INFINITY;
+            const float v = key < key_limit ? sacc[kb][r] : -INFINITY;
             sacc[kb][r] = v;
             tmax = fmaxf(tmax, v);
           }
@@ -351,14 +404,11 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float v = sacc[kb][r] * a.scale_log2;
-            sacc[kb][r] = v;
-            tmax = fmaxf(tmax, v);
-          }
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run, tmax);
+      const float m_tile = tmax == -INFINITY ? -INFINITY : tmax * a.scale_log2;
+      const float m_new = fmaxf(m_run, m_tile);
       const float m_ref = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
       m_run = m_new;
@@ -370,7 +420,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
         float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(sacc[kb][r] - m_ref);
+          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.scale_log2, -m_ref));
           psum += p[r];
         }
         frag_from_f32<DT>(pf[2 * kb], p);
@@ -403,21 +453,21 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 
   // Tile t is computed from LDS buffer t % 2 while tile t + 1 sits in staging registers
   // (its LDS write follows) and tile t + 2's global loads are in flight.
-  load_tile(0, kA, vA);
-  if (ntiles > 1) load_tile(1, kB, vB);
-  store_tile(0, kA, vA);
+  load_tile(0, stA);
+  load_tile(1, stB);
+  store_tile(0, 0, stA);
   __syncthreads();
-  if (ntiles > 2) load_tile(2, kA, vA);
+  load_tile(2, stA);
   for (int tile = 0; tile < ntiles; tile += 2) {
     compute_tile(tile, ks[0], vt[0]);
-    if (tile + 1 < ntiles) store_tile(1, kB, vB);
+    store_tile(1, tile + 1, stB);  // past the end: unread
     __syncthreads();
     if (tile + 1 >= ntiles) break;
-    if (tile + 3 < ntiles) load_tile(tile + 3, kB, vB);
+    load_tile(tile + 3, stB);
     compute_tile(tile + 1, ks[1], vt[1]);
-    if (tile + 2 < ntiles) store_tile(0, kA, vA);
+    store_tile(0, tile + 2, stA);
     __syncthreads();
-    if (tile + 4 < ntiles) load_tile(tile + 4, kA, vA);
+    load_tile(tile + 4, stA);
   }
 
   // Normalise and write.  O^T register r of tile dt is head_dim position
@@ -451,7 +501,10 @@ nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, i
     if (tiles <= 0) return NV_OK;
     grid = dim3(tiles, heads_y, num_seqs);
   }
-  paged_prefill_kernel<DT, D, GW, PB, BN><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
+  if (a.bs_shift >= 0)
+    paged_prefill_kernel<DT, D, GW, PB, BN, true><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
+  else
+    paged_prefill_kernel<DT, D, GW, PB, BN, false><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
   return nvp_host::launch_status();
 }
 
@@ -491,6 +544,9 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
       num_tiles < 0)
     return NV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return NV_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
+      softmax_scale == -INFINITY)
+    return NV_ERR_INVALID_ARG;
   if (dtype != NV_F32 && dtype != NV_BF16) return NV_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return NV_ERR_UNSUPPORTED;
   if (block_size % 16 != 0) return NV_ERR_UNSUPPORTED;
@@ -520,7 +576,13 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
   a.block_size = block_size;
   a.group = g;
   a.causal = causal ? 1 : 0;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.bs_shift = nvp_host::is_pow2(block_size) ? __builtin_ctz(static_cast<unsigned>(block_size)) : -1;
+  // The kernel takes a positive scale: a negative one flips the sign of q instead, and a
+  // zero scale becomes 1e-30 (every score times it rounds to 0, so each weight is
+  // exactly 2^0 = 1 as with scale 0, and masked keys stay at -inf).
+  a.negate_q = softmax_scale < 0.f ? 1 : 0;
+  const float mag = softmax_scale < 0.f ? -softmax_scale : softmax_scale;
+  a.scale_log2 = mag > 0.f ? mag * 1.4426950408889634f : 1e-30f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == NV_BF16)
     return head_dim == 128 ? dispatch_prefill<BF16, 128>(a, num_seqs, max_seqlen_q, num_tiles, s)

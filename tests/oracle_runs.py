@@ -32,7 +32,7 @@ class OracleDecode:
                                               self.case.shape.block_size)
         oracle.store_kvcache(self.kc, self.vc, st.k_new, st.v_new, slots)
 
-    def run_to(self, t: int, seqs=None):
+    def run_to(self, t: int, seqs=None, scale=None):
         """Store steps up to and including t, then decode step t (optionally only
         the sequences in ``seqs``).  Returns float64 [B or len(seqs), Hq, D]."""
         while self.next_step <= t:
@@ -41,11 +41,13 @@ class OracleDecode:
         st = self.case.steps[t]
         idx = np.arange(len(st.context_lens)) if seqs is None else np.asarray(seqs)
         return oracle.paged_decode(st.q[idx], self.kc, self.vc, st.block_tables[idx],
-                                   st.context_lens[idx], self.case.shape.scale)
+                                   st.context_lens[idx],
+                                   self.case.shape.scale if scale is None else scale)
 
 
-def oracle_prefill(case: PrefillCase, seqs=None):
-    """Store the prefix and the new rows through the oracle, then run its prefill.
+def oracle_prefill(case: PrefillCase, seqs=None, scale=None):
+    """Store the prefix and the new rows through the oracle, then run its prefill (with
+    the shape's 1/sqrt(head_dim) scale unless ``scale`` is given).
 
     Returns (out float64 [sum(num_new), Hq, D], kc, vc, metadata tuple)."""
     sh = case.shape
@@ -54,6 +56,6 @@ def oracle_prefill(case: PrefillCase, seqs=None):
                                    sh.block_size, case.pad_to)
     cu_q, cu_k, _, _, slots = meta
     oracle.store_kvcache(kc, vc, case.k_new, case.v_new, slots)
-    out = oracle.paged_prefill(case.q, kc, vc, cu_q, cu_k, case.block_tables, sh.scale,
-                               case.causal)
+    out = oracle.paged_prefill(case.q, kc, vc, cu_q, cu_k, case.block_tables,
+                               sh.scale if scale is None else scale, case.causal)
     return out, kc, vc, meta

@@ -42,7 +42,7 @@ PREFILL_SHAPES = [
     ("f32", 128, 32, 8, 256), ("f32", 128, 8, 8, 16), ("f32", 64, 8, 4, 16),
     ("f32", 64, 16, 2, 32), ("f32", 128, 4, 2, 64),
     ("bf16", 128, 32, 8, 256), ("bf16", 128, 16, 16, 16), ("bf16", 64, 16, 8, 32),
-    ("bf16", 128, 64, 8, 16),
+    ("bf16", 128, 64, 8, 16), ("bf16", 128, 16, 8, 48), ("f32", 64, 8, 2, 80),
 ]
 NEW = [1, 31, 32, 33, 0, 64, 65, 100, 127, 160]
 CACHED = [0, 5, 16, 0, 7, 256, 33, 0, 48, 300]
@@ -123,3 +123,22 @@ def test_gpu_decode_matches_gpu_prefill_last_row():
     nv_paged_prefill(out, s["q"], dev.kc, dev.vc, i32(cu_q, "cuda"), i32(cu_k, "cuda"), 1,
                      int(L.max()), s["tables"], sh.scale, True)
     assert_close(to_host_f64(out), dec, TOL["f32"], "decode vs prefill")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_prefill_negative_and_zero_scale(dtype, scale):
+    """A negative scale (applied as |scale| to -q) and a zero scale (uniform weights over
+    the visible keys) against the oracle's plain definition."""
+    from paged_kv_cache_319_amd import nv_paged_prefill
+    from paged_kv_cache_319_amd.harness import DevicePrefill, to_host_f64
+    banner(f"prefill scale={scale} {dtype}")
+    sh = Shape(dtype, 8, 2, 128, 16, 40, 0.5 if dtype == "bf16" else 1.0)
+    case = build_prefill("scale", sh, [5, 70, 33], [16, 0, 48], seed=21, pad_to=16)
+    dev = DevicePrefill(case)
+    dev.store()
+    out = torch.empty_like(dev.out)
+    nv_paged_prefill(out, dev.q, dev.kc, dev.vc, dev.cu_q, dev.cu_k, dev.max_q, dev.max_k,
+                     dev.tables, scale, True, tile_schedule=dev.tiles)
+    want = oracle_prefill(case, scale=scale)[0]
+    assert_close(to_host_f64(out), want, TOL[dtype], f"prefill scale {scale}")

@@ -119,8 +119,10 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     # decode: heads not divisible, head_dim 96, block_size 8, too-small workspace, batch 0
     args = lambda **kw: [kw.get("out", p), p, p, p, p, kw.get("W", 4), p, None, kw.get("maxlen", 64),
                          kw.get("B", 2), kw.get("hq", 4), kw.get("hkv", 2), kw.get("d", 128),
-                         8, kw.get("bs", 16), 0.1, kw.get("dt", 1), kw.get("ws", None),
+                         8, kw.get("bs", 16), kw.get("sc", 0.1), kw.get("dt", 1), kw.get("ws", None),
                          kw.get("wsn", 0), s]
+    assert lib.nv_paged_decode(*args(sc=float("nan"))) == -1
+    assert lib.nv_paged_decode(*args(sc=float("inf"))) == -1
     assert lib.nv_paged_decode(*args(hq=3)) == -1
     assert lib.nv_paged_decode(*args(d=96)) == -2
     assert lib.nv_paged_decode(*args(bs=8)) == -2
@@ -136,7 +138,10 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.nv_paged_decode_workspace_size(256, 16, 8, 128, 4096, 256, 1) == 0
     # prefill: causal with bad heads, unsupported dtype, zero sequences is a no-op
     pre = lambda **kw: [p, p, p, p, p, p, 16, 16, p, 4, kw.get("S", 2), None, 0,
-                        kw.get("hq", 4), 2, kw.get("d", 128), 8, 16, 0.1, 1, kw.get("dt", 1), s]
+                        kw.get("hq", 4), 2, kw.get("d", 128), 8, 16, kw.get("sc", 0.1), 1,
+                        kw.get("dt", 1), s]
+    assert lib.nv_paged_prefill(*pre(sc=float("nan"))) == -1
+    assert lib.nv_paged_prefill(*pre(sc=float("-inf"))) == -1
     assert lib.nv_paged_prefill(*pre(hq=5)) == -1
     assert lib.nv_paged_prefill(*pre(dt=3)) == -2
     assert lib.nv_paged_prefill(*pre(d=80)) == -2

@@ -30,6 +30,8 @@
 //   order in which the S^T accumulator holds the keys.
 // The contraction index of an MFMA may be permuted freely as long as A and B
 // agree, which is what lets P^T feed the second product without a shuffle.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -138,6 +140,21 @@ __device__ __forceinline__ void frag_from_f32<F32>(Frag<F32>& f, const float* x)
   for (int e = 0; e < 8; ++e) f.v[e / 4][e % 4] = __float_as_uint(x[e]);
 }
 
+// Two transposing 8-byte LDS reads (ds_read_b64_tr_b16) into one bf16 fragment.  Within
+// each group of 16 lanes, lane i receives element i % 4 of the pieces that lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 point at.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+__device__ __forceinline__ u32x4 tr_pair(const uint16_t* p0, const uint16_t* p1) {
+  // p0, p1 point into __shared__ memory: the casts are generic -> LDS address space.
+  const auto a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p0));
+  const auto b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p1));
+  const uint2 ua = __builtin_bit_cast(uint2, a);
+  const uint2 ub = __builtin_bit_cast(uint2, b);
+  return u32x4{ua.x, ua.y, ub.x, ub.y};
+}
+__device__ __forceinline__ u32x4 tr_pair(const float*, const float*) { return u32x4{0, 0, 0, 0}; }
+
 // Four output elements (consecutive head_dim positions) -> memory.
 template <typename DT>
 __device__ __forceinline__ void store4(typename DT::T* p, float a, float b, float c, float d);
@@ -197,7 +214,10 @@ struct PrefillArgs {
   float scale_log2;    // |softmax_scale| * log2(e), > 0
 };
 
-template <typename DT, int D, int GW, int PB, int BN, bool POW2>
+// BMODE: how a tile's keys find their cache blocks.  2: power-of-two block size >= BN (a
+// tile lies in one block); 1: smaller power-of-two blocks (a tile spans BN / block_size
+// blocks); 0: any other block size (each 4-key unit looks its block up).
+template <typename DT, int D, int GW, int PB, int BN, int BMODE>
 __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs a) {
   using T = typename DT::T;
   constexpr int ES = DT::kBytes;
@@ -208,7 +228,13 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   constexpr int NKB = BN / 32;           // 32-key blocks per tile
   constexpr int NKS = BN / 16;           // 16-key contraction slices per tile
   constexpr int KROW = D + EPC;          // padded K row (elements)
-  constexpr int VROW = BN + 4;           // padded transposed-V row (elements)
+  // bf16: V is kept row-major in LDS and read transposed (ds_read_b64_tr_b16); its rows
+  // are padded to 16 elements past head_dim so that the 16 lanes of one transposed read
+  // (4 rows x 32 bytes) fall in distinct banks.  fp32: V is transposed on the way into
+  // LDS, rows of BN + 4 keys.
+  constexpr bool TRV = DT::kBytes == 2;
+  constexpr int VROW = TRV ? D + 16 : BN + 4;
+  constexpr int VBUF = TRV ? BN * VROW : D * VROW;
   constexpr int UNITS = (BN / 4) * CPR;  // 4-key x 16-byte staging units per tile
   constexpr int NT = 64 * GW * PB;       // threads per workgroup
   constexpr int HALF = NT / 2;           // the first half stages K, the second V
@@ -217,7 +243,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 
   // Two K / V^T tile buffers: the next tile is written while this one is read.
   __shared__ __attribute__((aligned(16))) T ks[2][BN * KROW];
-  __shared__ __attribute__((aligned(16))) T vt[2][D * VROW];
+  __shared__ __attribute__((aligned(16))) T vt[2][VBUF];
 
   // Work tile: from the host schedule (grid = heads x tiles, heaviest tiles first), or
   // the dense grid (tiles x heads x sequences, a sequence's late tiles first).
@@ -279,72 +305,105 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   }
 
   // Staging registers: the first half of the workgroup's waves stages K, the second
-  // half V, UPT units (4 keys x one 16-byte chunk) per thread.  Two sets, so each tile's
-  // global loads are issued two tiles before its LDS write.  Every call issues the same
-  // loads (a tile past the end reads the pool's first element), which keeps the
+  // half V, UPT units (4 keys x one 16-byte chunk) per thread.  Every call issues the
+  // same loads (a tile past the end reads the pool's first element), which keeps the
   // compiler's count of loads in flight exact and its waits minimal.
   const bool v_role = wave >= (GW * PB) / 2;   // wave-uniform
   const int rtid = tid - (v_role ? HALF : 0);
   const T* __restrict__ src = v_role ? vc : kc;
-  u32x4 stA[UPT][4], stB[UPT][4];
+  u32x4 stA[UPT][4];
 
-  // A 4-key unit never straddles a block (the block size is a multiple of 16).  With a
-  // power-of-two block size the tile's BN keys span at most four blocks whose table
-  // entries are workgroup-uniform (scalar loads, which never wait on the vector loads in
-  // flight); otherwise each unit looks its block up itself.
+  // A 4-key unit never straddles a block (the block size is a multiple of 16).  Block
+  // lookups are workgroup-uniform scalar loads where the block size allows (they never
+  // wait on the vector loads in flight): one block per tile (BMODE 2, whose loads then
+  // take a uniform base address and a 32-bit lane offset) or the tile's BN / block_size
+  // blocks (BMODE 1); otherwise each unit looks its block up itself.  Keys at or past
+  // k_end read a valid row instead (the tile's first, or row 0 of block 0 for a tile
+  // wholly past the end); the LDS write replaces them by zero (V must be finite there:
+  // its weight is zero), which keeps these loads in flight until then.
   const int last_entry = a.max_blocks - 1;
+  const int my_c = rtid % CPR;                     // unit u adds HALF * u to rtid
   auto load_tile = [&](int tile, u32x4 (&st)[UPT][4]) {
-    int ent[4] = {0, 0, 0, 0};
-    if constexpr (POW2) {
-      const int lb0 = (tile * BN) >> a.bs_shift;
+    if constexpr (BMODE == 2) {
+      const int k0 = tile * BN;
+      const int blk = k0 < k_end ? bt[min(k0 >> a.bs_shift, last_entry)] : 0;
+      const int off0 = k0 < k_end ? (k0 & ((1 << a.bs_shift) - 1)) : 0;
+      const T* __restrict__ base =
+          src + (static_cast<int64_t>(blk) * a.block_size + off0) * slot_stride +
+          static_cast<int64_t>(j) * D;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ent[i] = bt[min(lb0 + i, last_entry)];
-    }
+      for (int u = 0; u < UPT; ++u) {
+        const int unit = rtid + HALF * u;
+        if (UNITS % HALF == 0 || unit < UNITS) {   // wave-uniform: UNITS is a multiple of 64
+          const int kg = unit / CPR;
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = rtid + HALF * u;
-      if (UNITS % HALF == 0 || unit < UNITS) {  // wave-uniform: UNITS is a multiple of 64
-        const int c = unit % CPR;
-        const int kg = unit / CPR;
-        const int kp0 = tile * BN + 4 * kg;     // first of the unit's four keys
-        int blk, off;
-        if constexpr (POW2) {
-          const int i = (4 * kg) >> a.bs_shift;  // 0 when the block holds the whole tile
-          blk = i == 0 ? ent[0] : i == 1 ? ent[1] : i == 2 ? ent[2] : ent[3];
-          off = kp0 & ((1 << a.bs_shift) - 1);
-        } else {
-          const int lb = min(kp0 / a.block_size, last_entry);
-          blk = bt[lb];
-          off = kp0 - lb * a.block_size;
+          for (int x = 0; x < 4; ++x) {
+            const uint32_t o = static_cast<uint32_t>((4 * kg + x) * slot_stride + my_c * EPC);
+            st[u][x] = load16(base + (k0 + 4 * kg + x < k_end ? o : 0u));
+          }
         }
-        const int64_t e0 = (static_cast<int64_t>(blk) * a.block_size + off) * slot_stride +
-                           static_cast<int64_t>(j) * D + c * EPC;
-        // Keys at or past k_end read element 0 of the pool instead; store_tile replaces
-        // them by zero (V must be finite there: its weight is zero).  Deferring that
-        // select keeps these loads in flight until the tile is written to LDS.
+      }
+    } else {
+      int ent[4] = {0, 0, 0, 0};
+      if constexpr (BMODE == 1) {
+        const int lb0 = (tile * BN) >> a.bs_shift;
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          st[u][x] = load16(src + (kp0 + x < k_end ? e0 + x * slot_stride : 0));
+        for (int i = 0; i < 4; ++i) ent[i] = bt[min(lb0 + i, last_entry)];
+      }
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int unit = rtid + HALF * u;
+        if (UNITS % HALF == 0 || unit < UNITS) {
+          const int c = unit % CPR;
+          const int kg = unit / CPR;
+          const int kp0 = tile * BN + 4 * kg;     // first of the unit's four keys
+          int blk, off;
+          if constexpr (BMODE == 1) {
+            const int i = (4 * kg) >> a.bs_shift;
+            blk = i == 0 ? ent[0] : i == 1 ? ent[1] : i == 2 ? ent[2] : ent[3];
+            off = kp0 & ((1 << a.bs_shift) - 1);
+          } else {
+            const int lb = min(kp0 / a.block_size, last_entry);
+            blk = bt[lb];
+            off = kp0 - lb * a.block_size;
+          }
+          const int64_t e0 = (static_cast<int64_t>(blk) * a.block_size + off) * slot_stride +
+                             static_cast<int64_t>(j) * D + c * EPC;
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            st[u][x] = load16(src + (kp0 + x < k_end ? e0 + x * slot_stride : 0));
+        }
       }
     }
   };
-  auto store_tile = [&](int buf, int tile, const u32x4 (&st)[UPT][4]) {
+  // LDS write of a staged tile: K rows as they are; V rows as they are (bf16) or
+  // transposed (fp32).  Only the tile holding k_end has keys to zero.
+  auto store_tile = [&](T* buf, int tile, const u32x4 (&st)[UPT][4]) {
+    const bool tail = (tile + 1) * BN > k_end;     // workgroup-uniform
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = rtid + HALF * u;
       if (UNITS % HALF == 0 || unit < UNITS) {
         const int c = unit % CPR;
         const int kg = unit / CPR;
-        const int kp0 = tile * BN + 4 * kg;
         u32x4 x4[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) x4[x] = kp0 + x < k_end ? st[u][x] : u32x4{0, 0, 0, 0};
+        for (int x = 0; x < 4; ++x) x4[x] = st[u][x];
+        if (tail) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (tile * BN + 4 * kg + x >= k_end) x4[x] = u32x4{0, 0, 0, 0};
+        }
         if (!v_role) {
 #pragma unroll
           for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x4*>(&ks[buf][(4 * kg + x) * KROW + c * EPC]) = x4[x];
+            *reinterpret_cast<u32x4*>(&buf[(4 * kg + x) * KROW + c * EPC]) = x4[x];
+        } else if constexpr (TRV) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            *reinterpret_cast<u32x4*>(&buf[(4 * kg + x) * VROW + c * EPC]) = x4[x];
         } else {
-          write_vt<DT>(vt[buf], VROW, c * EPC, 4 * kg, x4);
+          write_vt<DT>(buf, VROW, c * EPC, 4 * kg, x4);
         }
       }
     }
@@ -360,114 +419,164 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 
   const int qpos = p0 + q0 + qi;                        // absolute position of the query
   const int key_limit = a.causal ? min(qpos + 1, k_len) : k_len;
-  // Per wave: keys visible to every query row (no mask below this) and to any row.
-  const bool wave_active = q0 < n;
+  // Per wave: keys visible to every query row (no mask below this), keys visible to
+  // any row, and the number of tiles the wave computes.
   const int all_see = a.causal ? min(p0 + q0 + 1, k_len) : k_len;
   const int any_sees = a.causal ? p0 + min(q0 + 32, n) : k_len;
+  const int wtiles = q0 < n ? min(ntiles, (any_sees + BN - 1) / BN) : 0;
 
-  auto compute_tile = [&](int tile, const T* kst_lds, const T* vt_lds) {
-    if (wave_active && tile * BN < any_sees) {
-      // S^T = K Q^T for each 32-key block of the tile.
-      // The key blocks' accumulation chains are interleaved so consecutive MFMAs are
-      // independent.
-      f32x16 sacc[NKB];
+  // S^T = K Q^T for the 32-key blocks of one tile; the blocks' accumulation chains are
+  // interleaved so consecutive MFMAs are independent.
+  auto qk = [&](const T* kl, f32x16 (&sacc)[NKB]) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          Frag<DT> kf;
-          frag_load<DT>(kf, &kst_lds[(32 * kb + qi) * KROW + 16 * kk + 8 * hh]);
-          sacc[kb] = mma(kf, qf[kk], sacc[kb]);
-        }
-      }
-
-      // Mask (only where some key of the tile is hidden from some row) and tile maximum
-      // of the raw scores.  Register r of block kb holds key 32*kb + 8*(r/4) + 4*hh + r%4
-      // of the tile, for query column qi.  The scale (> 0) is applied inside the
-      // exponent: 2^(s*scale_log2 - m) with one fma per score.
-      float tmax = -INFINITY;
-      if ((tile + 1) * BN > all_see) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = tile * BN + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-            const float v = key < key_limit ? sacc[kb][r] : -INFINITY;
-            sacc[kb][r] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kb][r]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_tile = tmax == -INFINITY ? -INFINITY : tmax * a.scale_log2;
-      const float m_new = fmaxf(m_run, m_tile);
-      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-      m_run = m_new;
-
-      float psum = 0.f;
-      Frag<DT> pf[NKS];
+    for (int kk = 0; kk < KSTEPS; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.scale_log2, -m_ref));
-          psum += p[r];
-        }
-        frag_from_f32<DT>(pf[2 * kb], p);
-        frag_from_f32<DT>(pf[2 * kb + 1], p + 8);
-      }
-      l_run = l_run * alpha + psum;
-      // Rescale only when some query's maximum moved (alpha == 1 everywhere otherwise).
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-        for (int dt = 0; dt < DT32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-
-      // O^T += V^T P^T.  Fragment element e of slice ks holds key
-      // 16*ks + 8*(e/4) + 4*hh + e%4, matching the S^T register order above.  The
-      // head_dim tiles are the inner loop: their accumulators are independent.
-#pragma unroll
-      for (int ksl = 0; ksl < NKS; ++ksl) {
-#pragma unroll
-        for (int dt = 0; dt < DT32; ++dt) {
-          const T* vrow = &vt_lds[(32 * dt + qi) * VROW];
-          Frag<DT> vf;
-          frag_load_2x4<DT>(vf, vrow + 16 * ksl + 4 * hh, vrow + 16 * ksl + 8 + 4 * hh);
-          oacc[dt] = mma(vf, pf[ksl], oacc[dt]);
-        }
+        Frag<DT> kf;
+        frag_load<DT>(kf, &kl[(32 * kb + qi) * KROW + 16 * kk + 8 * hh]);
+        sacc[kb] = mma(kf, qf[kk], sacc[kb]);
       }
     }
   };
 
-  // Tile t is computed from LDS buffer t % 2 while tile t + 1 sits in staging registers
-  // (its LDS write follows) and tile t + 2's global loads are in flight.
-  load_tile(0, stA);
-  load_tile(1, stB);
-  store_tile(0, 0, stA);
+  // Online softmax, first half: mask (on tiles that cross the wave's diagonal) and the
+  // tile maximum.  Register r of block kb holds key 32*kb + 8*(r/4) + 4*hh + r%4 of the
+  // tile for query column qi; its partner lane (lane ^ 32) holds the other half of the
+  // keys, so the maximum costs one exchange.  The running maximum only moves when a
+  // tile exceeds it by more than 2^8 (weights then stay at most 256 and the rescale of
+  // O is rare); O and l always share one reference, so the softmax is unchanged.
+  // Returns the reference for the exponents; alpha is the rescale factor of O and l.
+  auto tile_max = [&](auto mask_c, int tile, f32x16 (&sacc)[NKB], float& alpha) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    // key = tile*BN + 32*kb + 8*(r/4) + 4*hh + r%4 is visible iff key < key_limit
+    const int lim = key_limit - tile * BN - 4 * hh;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASK)
+          sacc[kb][r] = 32 * kb + 8 * (r / 4) + (r % 4) < lim ? sacc[kb][r] : -INFINITY;
+        tmax = fmaxf(tmax, sacc[kb][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_tile = tmax == -INFINITY ? -INFINITY : tmax * a.scale_log2;
+    const float m_use = m_tile > m_run + 8.f ? m_tile : m_run;
+    const float m_ref = m_use == -INFINITY ? 0.f : m_use;
+    alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+    m_run = m_use;
+    return m_ref;
+  };
+
+  // Second half, fused with O^T += V^T P^T one 32-key block at a time: weights
+  // 2^(s*scale_log2 - m) (the scale, > 0, applied by one fma per score), their sum, the
+  // bf16 (or fp32) fragments, and the MFMAs over the block's two 16-key slices.
+  // Fragment element e of slice ks holds key 16*ks + 8*(e/4) + 4*hh + e%4, matching the
+  // S^T register order.  The head_dim tiles are the inner loop: their accumulators are
+  // independent.
+  const int tr_off = (4 * hh + ((lane & 15) >> 2)) * VROW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto softmax_pv = [&](const T* vl, const f32x16 (&sacc)[NKB], float m_ref) {
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], a.scale_log2, -m_ref));
+        psum += p[r];
+      }
+      Frag<DT> pf[2];
+      frag_from_f32<DT>(pf[0], p);
+      frag_from_f32<DT>(pf[1], p + 8);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int ksl = 2 * kb + h2;
+#pragma unroll
+        for (int dt = 0; dt < DT32; ++dt) {
+          Frag<DT> vf;
+          if constexpr (TRV) {
+            // Transposed reads: lane l gets V[key0 + 0..3][32*dt + l%32], key0 = 16*ksl
+            // + 4*hh (+ 8 for elements 4..7); each lane points its read at row key0 +
+            // (l%16)/4, columns 32*dt + 16*((l/16)%2) + 4*(l%4) .. +3.
+            const T* vb = vl + tr_off + (16 * ksl) * VROW + 32 * dt;
+            vf.v = tr_pair(vb, vb + 8 * VROW);
+          } else {
+            const T* vrow = &vl[(32 * dt + qi) * VROW];
+            frag_load_2x4<DT>(vf, vrow + 16 * ksl + 4 * hh, vrow + 16 * ksl + 8 + 4 * hh);
+          }
+          oacc[dt] = mma(vf, pf[h2], oacc[dt]);
+        }
+      }
+    }
+    l_run += psum;
+  };
+
+  // One tile step of a wave: the maximum of tile t's scores (in scur), the rare rescale
+  // of O, then one straight-line block with S of tile t + 1 (K from kl, into snext) and
+  // tile t's weights and P V (V from vl): the matrix cores and the vector ALUs work on
+  // independent data.
+  auto step = [&](int t, f32x16 (&scur)[NKB], f32x16 (&snext)[NKB], const T* kl,
+                  const T* vl) {
+    if (t >= wtiles) return;                       // wave-uniform
+    float alpha;
+    const float m_ref = (t + 1) * BN > all_see ? tile_max(std::true_type{}, t, scur, alpha)
+                                               : tile_max(std::false_type{}, t, scur, alpha);
+    l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    // On the wave's last tile this S is not needed; computing it anyway (from whatever
+    // finite values the buffer holds) keeps the block free of branches.
+    qk(kl, snext);
+    softmax_pv(vl, scur, m_ref);
+  };
+
+  // Tile pipeline.  In step t every wave reads K(t + 1) and V(t) from LDS; the K waves
+  // write K(t + 2) and the V waves V(t + 1) into the other buffers (the ones read in
+  // step t - 1), then issue the global loads of the tile they write in step t + 1, so
+  // each load has a whole step to arrive.  One barrier per step.
+  if (!v_role) {
+    load_tile(0, stA);
+    store_tile(ks[0], 0, stA);
+    load_tile(1, stA);
+    store_tile(ks[1], 1, stA);
+    load_tile(2, stA);
+  } else {
+    load_tile(0, stA);
+    store_tile(vt[0], 0, stA);
+    load_tile(1, stA);
+  }
   __syncthreads();
-  load_tile(2, stA);
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    compute_tile(tile, ks[0], vt[0]);
-    store_tile(1, tile + 1, stB);  // past the end: unread
+  f32x16 sA[NKB], sB[NKB];
+  if (wtiles > 0) qk(ks[0], sA);
+  __syncthreads();                                 // K(0) is overwritten in step 0
+  for (int t = 0; t < ntiles; t += 2) {
+    if (!v_role) {
+      store_tile(ks[0], t + 2, stA);
+      load_tile(t + 3, stA);
+    } else {
+      store_tile(vt[1], t + 1, stA);
+      load_tile(t + 2, stA);
+    }
+    step(t, sA, sB, ks[1], vt[0]);
     __syncthreads();
-    if (tile + 1 >= ntiles) break;
-    load_tile(tile + 3, stB);
-    compute_tile(tile + 1, ks[1], vt[1]);
-    store_tile(0, tile + 2, stA);
+    if (t + 1 >= ntiles) break;
+    if (!v_role) {
+      store_tile(ks[1], t + 3, stA);
+      load_tile(t + 4, stA);
+    } else {
+      store_tile(vt[0], t + 2, stA);
+      load_tile(t + 3, stA);
+    }
+    step(t + 1, sB, sA, ks[0], vt[1]);
     __syncthreads();
-    load_tile(tile + 4, stA);
   }
 
   // Normalise and write.  O^T register r of tile dt is head_dim position
@@ -501,10 +610,12 @@ nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, i
     if (tiles <= 0) return NV_OK;
     grid = dim3(tiles, heads_y, num_seqs);
   }
-  if (a.bs_shift >= 0)
-    paged_prefill_kernel<DT, D, GW, PB, BN, true><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
+  if (a.bs_shift >= 0 && (1 << a.bs_shift) >= BN)
+    paged_prefill_kernel<DT, D, GW, PB, BN, 2><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
+  else if (a.bs_shift >= 0)
+    paged_prefill_kernel<DT, D, GW, PB, BN, 1><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
   else
-    paged_prefill_kernel<DT, D, GW, PB, BN, false><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
+    paged_prefill_kernel<DT, D, GW, PB, BN, 0><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
   return nvp_host::launch_status();
 }
 

@@ -73,24 +73,6 @@ def decode_flops(step, shape):
 # GPU legs
 # ---------------------------------------------------------------------------
 
-def time_decode_steps(dev, steps_idx, torch, flush=None):
-    """Store then decode, two launches per step; per-step (store_ms, decode_ms) from HIP
-    events recorded on the stream the kernels are launched on."""
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in steps_idx]
-    for (a, b, c), t in zip(ev, steps_idx):
-        if flush is not None:
-            flush()
-        a.record(stream)
-        dev.store(t)
-        b.record(stream)
-        dev.decode(t)
-        c.record(stream)
-    torch.cuda.synchronize()
-    return [(a.elapsed_time(b), b.elapsed_time(c)) for a, b, c in ev]
-
-
 def time_fused_steps(dev, steps_idx, torch, flush=None, graphs=True):
     """Fused store + decode (nv_paged_decode_store), one launch per step, replayed from the
     step's captured HIP graph (or called eagerly); per-step ms from HIP events recorded on
@@ -172,17 +154,20 @@ def headline(args, torch, extra):
     if not args.no_extra:
         # The same fused steps replayed from per-step HIP graphs.
         dev.capture_graphs()
-        gr = np.array(time_fused_steps(dev, order[:50], torch, graphs=True))
-        extra["c3_fused_graph_replay_us"] = float(gr.mean() * 1e3)
-        # The same steps as two launches (nv_store_kvcache, then nv_paged_decode).
-        per = time_decode_steps(dev, order[:50], torch)
-        st_ms = np.array([p[0] for p in per])
-        de_ms = np.array([p[1] for p in per])
+        it = iter(order[:50])
+        extra["c3_fused_graph_replay_us"] = float(
+            time_region(lambda: dev.replay(next(it)), 50, torch) * 1e3)
+        # The same steps as two launches (nv_store_kvcache, then nv_paged_decode), each
+        # kind timed over back-to-back launches of the 50 steps.
+        it = iter(order[:50] * 2)
+        st_ms = time_region(lambda: dev.store(next(it)), 50, torch)
+        it = iter(order[:50])
+        de_ms = time_region(lambda: dev.decode(next(it)), 50, torch)
         db = np.array([acct[t][0] for t in order[:50]])
-        extra["c3_separate_store_us"] = float(st_ms.mean() * 1e3)
-        extra["c3_separate_decode_us"] = float(de_ms.mean() * 1e3)
-        extra["c3_separate_decode_gbs"] = float(db.sum() / (de_ms.sum() * 1e-3) / 1e9)
-        extra["c3_separate_store_gbs"] = float(store_bytes / (st_ms.mean() * 1e-3) / 1e9)
+        extra["c3_separate_store_us"] = float(st_ms * 1e3)
+        extra["c3_separate_decode_us"] = float(de_ms * 1e3)
+        extra["c3_separate_decode_gbs"] = float(db.mean() / (de_ms * 1e-3) / 1e9)
+        extra["c3_separate_store_gbs"] = float(store_bytes / (st_ms * 1e-3) / 1e9)
         # Cold-cache kernel times: reading a 1 GiB buffer between steps (outside the
         # events) leaves L2 and the 256 MB MALL holding only clean lines of that buffer.
         scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -197,6 +182,20 @@ def headline(args, torch, extra):
     return case, res
 
 
+def time_region(fn, reps, torch):
+    """Mean ms of one launch: `reps` back-to-back calls bracketed by one HIP event pair on
+    the stream they are launched on (per-launch event pairs would add their own overhead)."""
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def extra_decode(name, torch, reps=20):
     from workloads import decode_config
     from paged_kv_cache_319_amd.harness import DeviceDecode
@@ -206,10 +205,9 @@ def extra_decode(name, torch, reps=20):
     dev.store(0)
     for _ in range(3):
         dev.decode(0)
-    per = time_decode_steps(dev, [0] * reps, torch)
-    dec = np.array([p[1] for p in per])
-    out = {f"{name.lower()}_decode_us": float(np.median(dec) * 1e3),
-           f"{name.lower()}_decode_gbs": float(b / (np.median(dec) * 1e-3) / 1e9)}
+    ms = time_region(lambda: dev.decode(0), reps, torch)
+    out = {f"{name.lower()}_decode_us": float(ms * 1e3),
+           f"{name.lower()}_decode_gbs": float(b / (ms * 1e-3) / 1e9)}
     del dev
     torch.cuda.empty_cache()
     return out
@@ -229,26 +227,18 @@ def extra_prefill(torch, reps=20):
     n = case.num_new.astype(np.float64)
     p = case.num_cached.astype(np.float64)
     flops = 4.0 * sh.head_dim * sh.num_q_heads * float(np.sum(n * p + n * (n + 1) / 2))
-    stream = torch.cuda.current_stream()
-    evs = []
-    for _ in range(reps):
-        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record(stream)
+    for _ in range(3):
         dev.store()
-        b.record(stream)
         dev.attend()
-        c.record(stream)
-        evs.append((a, b, c))
-    torch.cuda.synchronize()
-    st = np.array([a.elapsed_time(b) for a, b, c in evs])
-    at = np.array([b.elapsed_time(c) for a, b, c in evs])
+    st = time_region(dev.store, reps, torch)    # the store is idempotent
+    at = time_region(dev.attend, reps, torch)
     rows = int(case.k_new.shape[0])
     sbytes = 2 * 2 * int(n.sum()) * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * rows
-    out = {"c5_prefill_us": float(np.median(at) * 1e3),
-           "c5_prefill_tflops": float(flops / (np.median(at) * 1e-3) / 1e12),
-           "c5_prefill_mfma_frac": float(flops / (np.median(at) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
-           "c5_store_us": float(np.median(st) * 1e3),
-           "c5_store_gbs": float(sbytes / (np.median(st) * 1e-3) / 1e9)}
+    out = {"c5_prefill_us": float(at * 1e3),
+           "c5_prefill_tflops": float(flops / (at * 1e-3) / 1e12),
+           "c5_prefill_mfma_frac": float(flops / (at * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
+           "c5_store_us": float(st * 1e3),
+           "c5_store_gbs": float(sbytes / (st * 1e-3) / 1e9)}
     del dev
     torch.cuda.empty_cache()
     return out

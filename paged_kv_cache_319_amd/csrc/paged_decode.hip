@@ -1,5 +1,5 @@
-// Paged GQA decode attention: length-scheduled work items, online softmax over
-// 256-token passes, split-K with a log-sum-exp merge for long contexts.
+// Paged GQA decode attention: length-scheduled work items, wave-local online softmax,
+// split-K with a log-sum-exp merge for long contexts.
 //
 // Operation (walkthrough, xingyun3d.csdn.net nano-vllm article, section 七;
 // softmax(Q K^T / sqrt(d)) V from "万字深度解析 Nano-vLLM", section 1.2): each
@@ -17,10 +17,10 @@
 // the tail.  One workgroup of NW waves walks its item in passes of TPW*NW
 // tokens; every lane issues all of its K and V loads of a pass (4 + 4
 // non-temporal 16-byte loads for bf16, head_dim 128: 16 tokens per wave)
-// before any arithmetic.  Short passes keep the kernel small (~80 VGPRs, six
-// waves per SIMD): while one workgroup computes, the others on the CU still
-// have loads in flight (batch-256 step: 64-token passes 92 us, 32-token 89.6 us,
-// 16-token 87.7 us, event-timed).
+// before any arithmetic.  Short passes keep the kernel small (~80-100 VGPRs):
+// while one workgroup computes, the others on the CU still have loads in flight
+// (batch-256 step: 64-token passes 92 us, 32-token 89.6 us, 16-token 87.7 us,
+// event-timed).  At most four workgroups share a CU (see launch_decode).
 //
 // Lanes.  A token row of head j (head_dim elements) is spread over LPT lanes of
 // 16 bytes, so one wave-wide load fetches TPL whole rows.  The g query heads of
@@ -28,10 +28,12 @@
 // from HBM once per step.
 //
 // Softmax.  Per pass: scores (v_dot2 for bf16, DPP reductions within LPT-lane
-// groups), each token's score kept in exactly one lane, the pass maximum across
-// waves through LDS, then an online update (running max m, sum l and P V
-// accumulator rescaled by 2^(m_old - m_new)).  Weights reach the P V loop
-// through LDS.  Scores carry a log2(e) factor so the exponentials are exp2.
+// groups), each token's score kept in exactly one lane, the wave's pass maximum,
+// then an online update of the wave's own state (running max m, sum l and P V
+// accumulator rescaled by 2^(m_old - m_new)).  The waves never wait for each other
+// inside the pass loop; their states are merged once at the end, each weighted by
+// 2^(m_wave - M).  Weights reach the P V loop through LDS.  Scores carry a log2(e)
+// factor so the exponentials are exp2.
 //
 // Split merge.  A chunk that covers a whole sequence writes the normalised
 // output.  Otherwise each chunk writes (m, l, o) partials to the workspace and
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   constexpr int PASS = TPW * NW;
   static_assert(ITERS % 4 == 0 && kWave % TPW == 0, "weights are read four at a time");
 
-  __shared__ float sm_max[2][NW][G];
+  __shared__ float sm_m[NW][G];
   __shared__ float sm_sum[NW][G];
   __shared__ __attribute__((aligned(16))) float sm_p[NW][G][kWave];
   __shared__ float sm_o[NW][G][D];
@@ -148,9 +150,9 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  int par = 0;
-  for (int ps = cs; ps < ce; ps += PASS, par ^= 1) {
+  for (int ps = cs; ps < ce; ps += PASS) {
     const int t0 = ps + wave * TPW;
+    if (t0 >= ce) break;  // wave-uniform; the loop has no workgroup barrier
     if (ps != cs) blk_wave = bt[min(block_of<FAST>(t0, a), last_entry)];
 
     // Issue every K and V load of this pass before any arithmetic.
@@ -198,28 +200,24 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       }
     }
     const bool valid = col < ITERS && (t0 + col * TPL + row) < ce;
+    // Online softmax per wave: the pass maximum of this wave (finite: its first token
+    // is valid).  The running maximum moves only when a pass exceeds it by more than 8
+    // (weights stay at most 2^8), so the rescale of the accumulators is rare; the waves'
+    // states are combined once, at the end.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       s[h] = valid ? s[h] * a.scale_log2 : -INFINITY;
       const float wm = group_max<kWave>(s[h]);
-      if (lane == 0) sm_max[par][wave][h] = wm;
-    }
-    __syncthreads();
-
-    // Online update with the workgroup maximum of this pass.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x = sm_max[par][0][h];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) x = fmaxf(x, sm_max[par][w][h]);
-      const float m_new = fmaxf(m_run[h], x);  // finite: the first token of a pass is valid
-      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
-      m_run[h] = m_new;
-      const float p = valid ? __builtin_amdgcn_exp2f(s[h] - m_new) : 0.f;
+      const float m_use = wm > m_run[h] + 8.f ? wm : m_run[h];
+      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_use);
+      m_run[h] = m_use;
+      const float p = valid ? __builtin_amdgcn_exp2f(s[h] - m_use) : 0.f;
       sm_p[wave][h][lane] = p;
       l_run[h] = l_run[h] * alpha + p;
+      if (alpha != 1.f) {  // wave-uniform
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -242,7 +240,9 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();  // sm_p is rewritten by the next pass
   }
 
-  // Fold the TPL rows of each wave, then the waves through LDS.
+  // Fold the TPL rows of each wave, then the waves through LDS, each weighted by
+  // 2^(m_wave - M) with M the largest wave maximum.  A wave that saw no token holds
+  // m = -inf and zero sums (weight 0); wave 0 always saw the chunk's first token.
   float lsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -258,7 +258,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) sm_sum[wave][h] = lsum[h];
+    for (int h = 0; h < G; ++h) {
+      sm_sum[wave][h] = lsum[h];
+      sm_m[wave][h] = m_run[h];
+    }
   }
   __syncthreads();
 
@@ -266,11 +269,15 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   const int64_t qrow0 = static_cast<int64_t>(b) * a.num_q_heads + qhead0;
   for (int idx = tid; idx < G * D; idx += 64 * NW) {
     const int h = idx / D, d = idx % D;
+    float M = sm_m[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
     float o = 0.f, l = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      o += sm_o[w][h][d];
-      l += sm_sum[w][h];
+      const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
+      o = fmaf(f, sm_o[w][h][d], o);
+      l = fmaf(f, sm_sum[w][h], l);
     }
     if (nchunks == 1) {
       store_out<DT>(outp + (qrow0 + h) * D + d, o / l);
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       const int64_t pidx = (qrow0 + h) * a.max_chunks + c;
       a.ws_o[pidx * D + d] = o;
       if (d == 0) {
-        a.ws_ml[pidx * 2] = m_run[h];
+        a.ws_ml[pidx * 2] = M;
         a.ws_ml[pidx * 2 + 1] = l;
       }
     }
@@ -338,17 +345,30 @@ Plan make_plan(int batch, int hq, int hkv, int d, int max_context_len) {
   return p;
 }
 
+// Shared memory of one decode workgroup (the kernel's arrays), and the total reserved
+// per workgroup: at most four workgroups (16 waves) share a CU's 160 KB.  Fewer
+// concurrent streams per CU read the head-strided K/V rows faster than the six
+// workgroups the registers would allow (measured on the batch-256, batch-64 and 32K
+// workloads: 2-8 % shorter decode).
+template <int D, int G, int NW>
+constexpr size_t decode_static_lds() {
+  return sizeof(float) * (2 * NW * G + NW * G * kWave + NW * G * D);
+}
+constexpr size_t kDecodeLdsPerWorkgroup = 36 * 1024;
+
 template <typename DT, int D, int G>
 nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.num_kv_heads, batch, a.max_chunks);
   const dim3 block(64 * kDecodeWaves);
+  static_assert(decode_static_lds<D, G, kDecodeWaves>() < kDecodeLdsPerWorkgroup, "LDS");
+  const size_t pad = kDecodeLdsPerWorkgroup - decode_static_lds<D, G, kDecodeWaves>();
   const bool fast = a.bs_shift >= 6;
   if (a.new_slots) {
-    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, true><<<grid, block, 0, s>>>(a);
-    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, true><<<grid, block, 0, s>>>(a);
+    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, true><<<grid, block, pad, s>>>(a);
+    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, true><<<grid, block, pad, s>>>(a);
   } else {
-    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, false><<<grid, block, 0, s>>>(a);
-    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, false><<<grid, block, 0, s>>>(a);
+    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, false><<<grid, block, pad, s>>>(a);
+    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, false><<<grid, block, pad, s>>>(a);
   }
   if (a.max_chunks > 1)
     decode_merge_kernel<DT, D><<<dim3(a.num_q_heads, batch), dim3(D), 0, s>>>(a);

@@ -536,6 +536,24 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
     // finite values the buffer holds) keeps the block free of branches.
     qk(kl, snext);
     softmax_pv(vl, scur, m_ref);
+    if constexpr (TRV) {
+      // Schedule of the block (bf16): six LDS reads ahead, then per S MFMA one K read
+      // and four vector instructions, per P V MFMA two V reads and three vector
+      // instructions, so LDS latency and the softmax arithmetic hide under the MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS read
+#pragma unroll
+      for (int i = 0; i < NKB * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // VALU
+      }
+#pragma unroll
+      for (int i = 0; i < NKS * DT32; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    }
   };
 
   // Tile pipeline.  In step t every wave reads K(t + 1) and V(t) from LDS; the K waves

@@ -83,6 +83,15 @@ __device__ __forceinline__ int block_of(int t, const DecodeArgs& a) {
   return FAST ? (t >> a.bs_shift) : (t / a.block_size);
 }
 
+// Returns x unchanged, held in a vector register: the compiler then treats it as
+// varying over the wave, so a load from an address built on it is a vector memory load
+// rather than a scalar one.  Used for the per-pass block-table entry, which measured
+// faster through the vector path (4 % on the 32 K-context split decode).
+__device__ __forceinline__ int in_vgpr(int x) {
+  asm("" : "+v"(x));
+  return x;
+}
+
 template <typename DT, int D, int G, int NW, bool FAST, bool STORE>
 __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   using T = typename DT::T;
@@ -135,11 +144,18 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   const int nchunks = min((L + a.chunk - 1) / a.chunk, a.max_chunks);
 
   // Fused store: the K/V row of the decoded token (position L - 1) comes from this
-  // step's input and is written to its cache slot.  Only this workgroup reads that
-  // row of head j, and it reads it from the input, so the write cannot race a read.
-  const T* __restrict__ kn = static_cast<const T*>(a.k_new) + static_cast<int64_t>(b) * a.k_new_stride + head_off;
-  const T* __restrict__ vn = static_cast<const T*>(a.v_new) + static_cast<int64_t>(b) * a.v_new_stride + head_off;
+  // step's input.  In the chunk that holds it, row 0 of wave 0 loads that row of head j
+  // here, and after the loop writes it to its cache slot and adds the token to wave 0's
+  // softmax state; the loop itself covers the cached tokens [cs, ce_c) only.  No other
+  // workgroup reads that row of head j, so the write races no read.
   const int pos_new = (STORE && slot_new >= 0) ? L - 1 : -1;
+  const bool new_here = STORE && pos_new >= cs && pos_new < ce;
+  const int ce_c = new_here ? pos_new : ce;
+  u32x4 kn_r = u32x4{0, 0, 0, 0}, vn_r = u32x4{0, 0, 0, 0};
+  if (new_here && wave == 0 && row == 0) {
+    kn_r = load16(static_cast<const T*>(a.k_new) + static_cast<int64_t>(b) * a.k_new_stride + head_off);
+    vn_r = load16(static_cast<const T*>(a.v_new) + static_cast<int64_t>(b) * a.v_new_stride + head_off);
+  }
 
   float m_run[G], l_run[G], acc[G][EPL];
 #pragma unroll
@@ -150,10 +166,10 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  for (int ps = cs; ps < ce; ps += PASS) {
+  for (int ps = cs; ps < ce_c; ps += PASS) {
     const int t0 = ps + wave * TPW;
-    if (t0 >= ce) break;  // wave-uniform; the loop has no workgroup barrier
-    if (ps != cs) blk_wave = bt[min(block_of<FAST>(t0, a), last_entry)];
+    if (t0 >= ce_c) break;  // wave-uniform; the loop has no workgroup barrier
+    if (ps != cs) blk_wave = bt[in_vgpr(min(block_of<FAST>(t0, a), last_entry))];
 
     // Issue every K and V load of this pass before any arithmetic.
     u32x4 kr[ITERS], vr[ITERS];
@@ -171,20 +187,13 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       }
       kr[i] = u32x4{0, 0, 0, 0};
       vr[i] = u32x4{0, 0, 0, 0};
-      if (tf + row < ce) {
+      if (tf + row < ce_c) {
         const int64_t slot = static_cast<int64_t>(blk) * a.block_size + off + row;
         const int64_t e = slot * slot_stride + head_off;
-        const bool is_new = STORE && tf + row == pos_new;
-        kr[i] = load16_stream(is_new ? kn : kc + e);
-        vr[i] = load16_stream(is_new ? vn : vc + e);
+        kr[i] = load16_stream(kc + e);
+        vr[i] = load16_stream(vc + e);
       }
     }
-    if (STORE && pos_new >= t0 && pos_new < t0 + TPW && (pos_new - t0) % TPL == row) {
-      const int64_t e = static_cast<int64_t>(slot_new) * slot_stride + head_off;
-      *reinterpret_cast<u32x4*>(const_cast<T*>(kc) + e) = load16(kn);
-      *reinterpret_cast<u32x4*>(const_cast<T*>(vc) + e) = load16(vn);
-    }
-
     // Scores.  After the group reduction all LPT lanes of a row hold the dot
     // product; lane (row, col == i) keeps iteration i's score (lanes with
     // col >= ITERS keep none).
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
         s[h] = (col == i) ? part : s[h];
       }
     }
-    const bool valid = col < ITERS && (t0 + col * TPL + row) < ce;
+    const bool valid = col < ITERS && (t0 + col * TPL + row) < ce_c;
     // Online softmax per wave: the pass maximum of this wave (finite: its first token
     // is valid).  The running maximum moves only when a pass exceeds it by more than 8
     // (weights stay at most 2^8), so the rescale of the accumulators is rare; the waves'
@@ -240,9 +249,33 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();  // sm_p is rewritten by the next pass
   }
 
+  if (new_here && wave == 0) {  // wave-uniform: the decoded token
+    if (row == 0) {
+      const int64_t e = static_cast<int64_t>(slot_new) * slot_stride + head_off;
+      *reinterpret_cast<u32x4*>(const_cast<T*>(kc) + e) = kn_r;
+      *reinterpret_cast<u32x4*>(const_cast<T*>(vc) + e) = vn_r;
+    }
+    float vv[EPL];
+    widen<DT>(vn_r, vv);  // zero outside row 0
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      // Row 0 holds the score after the group reduction; lane 0 broadcasts it.
+      const float part = group_sum<LPT>(dot16<DT>(kn_r, qr[h], 0.f)) * a.scale_log2;
+      const float sn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(part)));
+      const float m_new = fmaxf(m_run[h], sn);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);  // 0 if no cached token
+      const float p = __builtin_amdgcn_exp2f(sn - m_new);
+      m_run[h] = m_new;
+      l_run[h] = l_run[h] * alpha + (lane == 0 ? p : 0.f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vv[e], acc[h][e] * alpha);
+    }
+  }
+
   // Fold the TPL rows of each wave, then the waves through LDS, each weighted by
   // 2^(m_wave - M) with M the largest wave maximum.  A wave that saw no token holds
-  // m = -inf and zero sums (weight 0); wave 0 always saw the chunk's first token.
+  // m = -inf and zero sums (weight 0); wave 0 always holds a token: the chunk's first
+  // cached one, or the decoded one when that is the chunk's only token.
   float lsum[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {

@@ -214,16 +214,42 @@ def extra_decode(name, torch, reps=20):
     return out
 
 
-def extra_prefill(torch, reps=20):
+def extra_block_size(bs, torch):
+    """The batch-256 workload redrawn with block size `bs` (same lengths, pool bytes and
+    shared 256-token prefixes): fused store + decode, one warm pass over the 50 steps,
+    then one timed pass, back to back."""
+    from workloads import decode_config
+    from paged_kv_cache_319_amd.harness import DeviceDecode
+    case = decode_config("C3", block_size=bs)
+    dev = DeviceDecode(case, poison=False)
+    nst = len(case.steps)
+    alg = np.array([decode_bytes(st, case.shape)[0] for st in case.steps])
+    for t in range(nst):
+        dev.step_fused(t)
+    state = {"t": 0}
+
+    def one():
+        dev.step_fused(state["t"] % nst)
+        state["t"] += 1
+    ms = time_region(one, nst, torch)
+    out = {f"c3_bs{bs}_fused_us": float(ms * 1e3),
+           f"c3_bs{bs}_fused_gbs": float(alg.mean() / (ms * 1e-3) / 1e9)}
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_prefill(torch, reps=20, bs=None):
     from workloads import prefill_config
     from paged_kv_cache_319_amd.harness import DevicePrefill
-    case = prefill_config()
+    case = prefill_config(block_size=bs)
+    tag = "c5" if bs is None else f"c5_bs{bs}"
     try:
         dev = DevicePrefill(case, poison=True)
         dev.store()
         dev.attend()
     except Exception as e:  # prefill not available: report, do not fail the bench
-        return {"c5_prefill_error": str(e)}
+        return {f"{tag}_prefill_error": str(e)}
     sh = case.shape
     n = case.num_new.astype(np.float64)
     p = case.num_cached.astype(np.float64)
@@ -235,11 +261,11 @@ def extra_prefill(torch, reps=20):
     at = time_region(dev.attend, reps, torch)
     rows = int(case.k_new.shape[0])
     sbytes = 2 * 2 * int(n.sum()) * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * rows
-    out = {"c5_prefill_us": float(at * 1e3),
-           "c5_prefill_tflops": float(flops / (at * 1e-3) / 1e12),
-           "c5_prefill_mfma_frac": float(flops / (at * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
-           "c5_store_us": float(st * 1e3),
-           "c5_store_gbs": float(sbytes / (st * 1e-3) / 1e9)}
+    out = {f"{tag}_prefill_us": float(at * 1e3),
+           f"{tag}_prefill_tflops": float(flops / (at * 1e-3) / 1e12),
+           f"{tag}_prefill_mfma_frac": float(flops / (at * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
+           f"{tag}_store_us": float(st * 1e3),
+           f"{tag}_store_gbs": float(sbytes / (st * 1e-3) / 1e9)}
     del dev
     torch.cuda.empty_cache()
     return out
@@ -368,6 +394,10 @@ def main():
             extra.update(extra_decode(name, torch))
         print("[bench] extra prefill C5", file=sys.stderr, flush=True)
         extra.update(extra_prefill(torch))
+        for bs in (16, 64):
+            print(f"[bench] extra block size {bs}", file=sys.stderr, flush=True)
+            extra.update(extra_block_size(bs, torch))
+        extra.update(extra_prefill(torch, bs=16))
     extra.update({k: res[k] for k in ("kernel_us_mean", "per_launch_event_us_p10",
                                       "per_launch_event_us_p50", "per_launch_event_us_p90",
                                       "effective_kv_gbs", "tflops", "kernel_tokens_per_s",

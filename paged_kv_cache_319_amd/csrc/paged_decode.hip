@@ -76,8 +76,16 @@ struct DecodeArgs {
   float scale_log2;
 };
 
+// Token rows one wave covers per pass: LPT = D / (16 / sizeof(T)) lanes hold one row,
+// a wave load covers 64 / LPT rows, and each lane issues max(LPT / 4, 4) loads.
+template <typename DT, int D>
+constexpr int decode_tokens_per_wave_pass() {
+  return (D / DT::kPerLoad >= 16 ? D / DT::kPerLoad / 4 : 4) * (kWave / (D / DT::kPerLoad));
+}
+
 // Logical block of token t (the paging article's t / B).  FAST: the block size is a
-// power of two and a multiple of 64, so a wave's 64 tokens never straddle a block.
+// power of two no smaller than the tokens of a wave-pass; passes start at multiples of
+// that count, so a wave-pass never straddles a block and needs one table entry.
 template <bool FAST>
 __device__ __forceinline__ int block_of(int t, const DecodeArgs& a) {
   return FAST ? (t >> a.bs_shift) : (t / a.block_size);
@@ -100,6 +108,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   constexpr int TPL = kWave / LPT;   // token rows per wave load
   constexpr int ITERS = LPT >= 16 ? LPT / 4 : 4;  // loads per lane per pass (K and V each)
   constexpr int TPW = ITERS * TPL;   // tokens per wave per pass: 16 or 32
+  static_assert(TPW == decode_tokens_per_wave_pass<DT, D>(), "pass geometry");
   constexpr int PASS = TPW * NW;
   static_assert(ITERS % 4 == 0 && kWave % TPW == 0, "weights are read four at a time");
 
@@ -395,7 +404,7 @@ nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
   const dim3 block(64 * kDecodeWaves);
   static_assert(decode_static_lds<D, G, kDecodeWaves>() < kDecodeLdsPerWorkgroup, "LDS");
   const size_t pad = kDecodeLdsPerWorkgroup - decode_static_lds<D, G, kDecodeWaves>();
-  const bool fast = a.bs_shift >= 6;
+  const bool fast = a.bs_shift >= 0 && (1 << a.bs_shift) >= decode_tokens_per_wave_pass<DT, D>();
   if (a.new_slots) {
     if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, true><<<grid, block, pad, s>>>(a);
     else paged_decode_kernel<DT, D, G, kDecodeWaves, false, true><<<grid, block, pad, s>>>(a);

@@ -174,14 +174,14 @@ def _blocks_for(length: int, block_size: int) -> int:
 
 def build_decode(name: str, shape: Shape, lengths0: Sequence[int], *, seed: int,
                  steps: int = 1, num_sharers: int = 0, max_shared_blocks: int = 2,
-                 table_width: Optional[int] = None) -> DecodeCase:
+                 share_unit: int = 1, table_width: Optional[int] = None) -> DecodeCase:
     """A decode workload of ``steps`` successive steps.
 
     Step t decodes one token per sequence with context length L0 + t; the token's
     own K/V row (position L0 + t - 1) is a new row.  When that position opens a
     new block, one block is popped from the free list.  ``num_sharers``
     sequences reference the same leading full blocks (1 .. ``max_shared_blocks``
-    of them, never the block the first write lands in).
+    units of ``share_unit`` blocks, never the block the first write lands in).
     """
     ss = np.random.SeedSequence(seed)
     r_struct, r_kv, r_q = [np.random.default_rng(s) for s in ss.spawn(3)]
@@ -198,12 +198,13 @@ def build_decode(name: str, shape: Shape, lengths0: Sequence[int], *, seed: int,
     n_sh = np.zeros(B, dtype=np.int64)
     shared: List[int] = []
     if num_sharers:
-        eligible = np.nonzero((lengths0 - 1) // bs >= 1)[0]
+        unit = bs * share_unit
+        eligible = np.nonzero((lengths0 - 1) // unit >= 1)[0]
         if len(eligible) < num_sharers:
             raise ValueError("not enough sequences long enough to share a full block")
         sharers = np.sort(r_struct.choice(eligible, size=num_sharers, replace=False))
         want = r_struct.integers(1, max_shared_blocks, endpoint=True, size=num_sharers)
-        n_sh[sharers] = np.minimum(want, (lengths0[sharers] - 1) // bs)
+        n_sh[sharers] = np.minimum(want, (lengths0[sharers] - 1) // unit) * share_unit
         shared = [free.pop() for _ in range(int(n_sh.max()))]
 
     tables = np.full((B, W), -1, dtype=np.int32)
@@ -317,14 +318,21 @@ SHAPES = {
 
 
 def decode_config(name: str, *, batch: Optional[int] = None, steps: Optional[int] = None,
-                  num_blocks: Optional[int] = None, seed: Optional[int] = None) -> DecodeCase:
+                  num_blocks: Optional[int] = None, seed: Optional[int] = None,
+                  block_size: Optional[int] = None) -> DecodeCase:
     """C1-C4.  ``batch``/``steps``/``num_blocks`` shrink a workload for CPU-sized tests
-    (same recipe, smaller draw); the defaults are the full workloads."""
+    (same recipe, smaller draw); the defaults are the full workloads.
+
+    ``block_size`` redraws the workload with another block size: the same lengths and
+    pool bytes (``num_blocks`` scaled by the size ratio unless given), and C3's shared
+    prefixes cover the same 1-2 x 256 tokens (as whole blocks of the new size)."""
     idx = CONFIG_NAMES.index(name)
     sh = SHAPES[name]
-    if num_blocks is not None:
-        sh = Shape(sh.dtype, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, sh.block_size,
-                   num_blocks, sh.sigma)
+    bs = sh.block_size if block_size is None else int(block_size)
+    if bs < 1 or (sh.block_size * sh.num_blocks) % bs:
+        raise ValueError(f"block size {bs} does not divide the {name} pool")
+    nb = num_blocks if num_blocks is not None else sh.block_size * sh.num_blocks // bs
+    sh = Shape(sh.dtype, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, bs, nb, sh.sigma)
     seed = 1000 + idx if seed is None else seed
     len_rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
     if name == "C1":
@@ -339,7 +347,8 @@ def decode_config(name: str, *, batch: Optional[int] = None, steps: Optional[int
         lengths = len_rng.integers(100, 1024, endpoint=True, size=B)
         n_share = int(round(0.3 * B))
         return build_decode(name, sh, lengths, seed=seed, steps=steps or 50,
-                            num_sharers=n_share, max_shared_blocks=2)
+                            num_sharers=n_share, max_shared_blocks=2,
+                            share_unit=max(1, 256 // bs))
     if name == "C4":
         B = batch or 8
         return build_decode(name, sh, [32768] * B, seed=seed, steps=steps or 1)
@@ -347,13 +356,22 @@ def decode_config(name: str, *, batch: Optional[int] = None, steps: Optional[int
 
 
 def prefill_config(name: str = "C5", *, num_seqs: Optional[int] = None,
-                   max_new: int = 1024, seed: Optional[int] = None) -> PrefillCase:
+                   max_new: int = 1024, seed: Optional[int] = None,
+                   block_size: Optional[int] = None) -> PrefillCase:
+    """C5.  ``block_size`` redraws it with another block size: the same lengths, prefixes
+    of 0-4 x 256 tokens and pool bytes."""
     if name != "C5":
         raise ValueError(f"{name} is not a prefill workload")
     sh = SHAPES[name]
+    if block_size is not None:
+        bs = int(block_size)
+        if bs < 1 or 256 % bs or (sh.block_size * sh.num_blocks) % bs:
+            raise ValueError(f"block size {bs} does not divide the C5 prefixes")
+        sh = Shape(sh.dtype, sh.num_q_heads, sh.num_kv_heads, sh.head_dim, bs,
+                   sh.block_size * sh.num_blocks // bs, sh.sigma)
     seed = 1000 + CONFIG_NAMES.index(name) if seed is None else seed
     S = num_seqs or 16
     len_rng = np.random.default_rng(np.random.SeedSequence([seed, 7]))
     n = len_rng.integers(min(100, max_new), max_new, endpoint=True, size=S)
-    p = sh.block_size * len_rng.integers(0, 4, endpoint=True, size=S)
+    p = 256 * len_rng.integers(0, 4, endpoint=True, size=S)
     return build_prefill(name, sh, n, p, seed=seed, pad_to=128, causal=True)

@@ -14,7 +14,14 @@ the method computes, as described on the nano-vLLM pages:
   * "deep dive" = "万字深度解析 Nano-vLLM" (chenxutan.com), sections 1.2 and 3.2.1;
   * "gitcode summary" = the gitcode.csdn.net nano-vLLM summary, section 三.4.
 
-Every function below is pinned by CPU tests against brute force, closed forms,
+``oracle.block_manager`` restates the walkthrough's section 五 block manager (ref
+counts, rolling-hash prefix reuse of full blocks, may_append, deallocate) in plain
+Python; its hash step calls the xxhash library's XXH64.  It is pinned by hand-worked
+traces, a published XXH64 digest and brute-force invariants over random traces
+(tests/test_block_manager_oracle.py, with planted mistakes in
+tests/test_block_manager_mutants.py).
+
+Every attention function below is pinned by CPU tests against brute force, closed forms,
 invariants and a library special case (torch's scaled_dot_product_attention in
 float64); none is "parity unpinned".
 """

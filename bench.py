@@ -239,6 +239,46 @@ def extra_block_size(bs, torch):
     return out
 
 
+def extra_block_manager():
+    """Host cost of the C++ block manager on the batch-256 shape: 256 prompts of
+    U[100, 1024] tokens (30 % sharing a 512-token stem) allocated in one prefill step,
+    then 50 decode steps, each appending one token per sequence and writing the step's
+    block tables, lengths and slots (block size 256, 2048 blocks)."""
+    import time
+    from paged_kv_cache_319_amd import BlockManager, _native
+    rng = np.random.default_rng(1003)
+    stem = rng.integers(0, 32000, size=512)
+    lens = rng.integers(100, 1024, endpoint=True, size=256)
+    prompts = []
+    for i, n in enumerate(lens):
+        p = rng.integers(0, 32000, size=int(n))
+        if i % 10 < 3 and n > 512:
+            p[:512] = stem
+        prompts.append(p)
+    bm = BlockManager(2048, 256)
+    t0 = time.perf_counter()
+    _, cached = bm.prefill_step(list(range(256)), prompts, 6)
+    t1 = time.perf_counter()
+    lib = _native.load()
+    ids = np.arange(256, dtype=np.int64)
+    toks = rng.integers(0, 32000, size=(50, 256)).astype(np.int32)
+    tables = np.zeros((256, 6), dtype=np.int32)
+    ctx = np.zeros(256, dtype=np.int32)
+    slots = np.zeros(256, dtype=np.int32)
+    ptrs = [a.ctypes.data_as(_native.c_i32p) for a in (tables, ctx, slots)]
+    t2 = time.perf_counter()
+    for step in range(50):
+        st = lib.nv_bm_decode_step(bm._h, ids.ctypes.data_as(_native.c_i64p),
+                                   toks[step].ctypes.data_as(_native.c_i32p), 256, ptrs[0], 6,
+                                   ptrs[1], ptrs[2])
+        if st != 0:
+            raise RuntimeError(f"nv_bm_decode_step failed ({st})")
+    t3 = time.perf_counter()
+    return {"block_manager_prefill_step_ms": float((t1 - t0) * 1e3),
+            "block_manager_cached_tokens": int(cached.sum()),
+            "block_manager_decode_step_us": float((t3 - t2) / 50 * 1e6)}
+
+
 def extra_prefill(torch, reps=20, bs=None):
     from workloads import prefill_config
     from paged_kv_cache_319_amd.harness import DevicePrefill
@@ -398,6 +438,7 @@ def main():
             print(f"[bench] extra block size {bs}", file=sys.stderr, flush=True)
             extra.update(extra_block_size(bs, torch))
         extra.update(extra_prefill(torch, bs=16))
+        extra.update(extra_block_manager())
     extra.update({k: res[k] for k in ("kernel_us_mean", "per_launch_event_us_p10",
                                       "per_launch_event_us_p50", "per_launch_event_us_p90",
                                       "effective_kv_gbs", "tflops", "kernel_tokens_per_s",

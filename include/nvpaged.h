@@ -31,7 +31,9 @@
  *     num_q_heads a multiple of num_kv_heads with at most 8 query heads per KV head.
  *   - Every pointer is caller-owned.  Device pointers must be device memory (for
  *     example from a PyTorch tensor); host pointers are ordinary host memory.
- *     The library keeps no state between calls and allocates no memory.
+ *     The entry points of this header keep no state between calls and allocate
+ *     no memory.  (The host-side block manager of nvpaged_blocks.h keeps its
+ *     state in host memory behind a handle the caller creates and destroys.)
  *   - GPU entry points enqueue work on `stream` (a hipStream_t; NULL = the null
  *     stream) and return without synchronising.  Host-checkable argument errors
  *     are reported before anything is enqueued; a failed launch returns
@@ -54,7 +56,8 @@ typedef enum nv_status {
   NV_ERR_INVALID_ARG = -1,          /* null pointer, negative size, inconsistent sizes */
   NV_ERR_UNSUPPORTED = -2,          /* head_dim / block_size / dtype / group size not built */
   NV_ERR_WORKSPACE_TOO_SMALL = -3,  /* decode workspace smaller than the size query */
-  NV_ERR_HIP = -4                   /* a HIP launch or runtime call failed */
+  NV_ERR_HIP = -4,                  /* a HIP launch or runtime call failed */
+  NV_ERR_OUT_OF_BLOCKS = -5         /* block manager: too few free blocks (nvpaged_blocks.h) */
 } nv_status;
 
 typedef enum nv_dtype {

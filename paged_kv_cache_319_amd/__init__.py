@@ -12,4 +12,5 @@ from .api import (  # noqa: F401
     nv_paged_prefill, nv_paged_prefill_tile_rows, nv_prepare_decode, nv_prepare_prefill,
     decode_workspace,
 )
+from .blocks import BlockManager, nv_bm_xxh64  # noqa: F401
 from ._native import LIB_PATH, load as load_library  # noqa: F401

@@ -7,6 +7,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvpaged.so")
 
 c_i32p = ctypes.POINTER(ctypes.c_int32)
+c_i64p = ctypes.POINTER(ctypes.c_int64)
 
 # name -> (restype, argtypes); mirrors include/nvpaged.h
 SIGNATURES = {
@@ -46,6 +47,27 @@ SIGNATURES = {
         c_i32p, ctypes.c_int32, c_i32p, c_i32p, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, c_i32p, c_i32p, c_i32p, c_i32p, c_i32p,
         ctypes.c_int32, c_i32p, ctypes.c_int32, c_i32p, ctypes.c_int32, c_i32p]),
+    # host-side block manager (include/nvpaged_blocks.h)
+    "nv_bm_create": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_void_p)]),
+    "nv_bm_destroy": (None, [ctypes.c_void_p]),
+    "nv_bm_num_free_blocks": (ctypes.c_int32, [ctypes.c_void_p]),
+    "nv_bm_can_allocate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_i32p]),
+    "nv_bm_allocate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, c_i32p, ctypes.c_int32,
+                                      c_i32p]),
+    "nv_bm_can_append": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, c_i32p]),
+    "nv_bm_append_token": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32]),
+    "nv_bm_deallocate": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64]),
+    "nv_bm_get_sequence": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, c_i32p, c_i32p,
+                                          c_i32p, ctypes.c_int32, c_i32p]),
+    "nv_bm_get_block": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, c_i32p, c_i32p,
+                                       ctypes.POINTER(ctypes.c_uint64)]),
+    "nv_bm_get_free_blocks": (ctypes.c_int, [ctypes.c_void_p, c_i32p, ctypes.c_int32, c_i32p]),
+    "nv_bm_decode_step": (ctypes.c_int, [ctypes.c_void_p, c_i64p, c_i32p, ctypes.c_int32,
+                                         c_i32p, ctypes.c_int32, c_i32p, c_i32p]),
+    "nv_bm_prefill_step": (ctypes.c_int, [ctypes.c_void_p, c_i64p, c_i32p, c_i32p,
+                                          ctypes.c_int32, c_i32p, ctypes.c_int32, c_i32p]),
+    "nv_bm_xxh64": (ctypes.c_uint64, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64]),
 }
 
 _lib = None

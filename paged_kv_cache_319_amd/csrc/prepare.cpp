@@ -36,6 +36,7 @@ extern "C" const char* nv_status_string(nv_status status) {
     case NV_ERR_UNSUPPORTED: return "unsupported configuration";
     case NV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case NV_ERR_HIP: return "HIP runtime error";
+    case NV_ERR_OUT_OF_BLOCKS: return "not enough free KV blocks";
   }
   return "unknown status";
 }

@@ -561,11 +561,15 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   // step t - 1), then issue the global loads of the tile they write in step t + 1, so
   // each load has a whole step to arrive.  One barrier per step.
   if (!v_role) {
+    // The K waves fill two buffers before the first barrier: a second staging set,
+    // live only here, puts tiles 0 and 1 in flight together (one memory latency at
+    // the start of the workgroup instead of two).
+    u32x4 stB[UPT][4];
     load_tile(0, stA);
+    load_tile(1, stB);
     store_tile(ks[0], 0, stA);
-    load_tile(1, stA);
-    store_tile(ks[1], 1, stA);
     load_tile(2, stA);
+    store_tile(ks[1], 1, stB);
   } else {
     load_tile(0, stA);
     store_tile(vt[0], 0, stA);

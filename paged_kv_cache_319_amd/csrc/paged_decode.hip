@@ -396,14 +396,19 @@ template <int D, int G, int NW>
 constexpr size_t decode_static_lds() {
   return sizeof(float) * (2 * NW * G + NW * G * kWave + NW * G * D);
 }
+// LDS reserved per workgroup, which caps how many share a CU: 36 KB (four) when every
+// sequence is one work item, 28 KB (five) when the plan splits sequences into chunks
+// (shorter items, whose start and end latencies more resident workgroups hide).
 constexpr size_t kDecodeLdsPerWorkgroup = 36 * 1024;
+constexpr size_t kDecodeLdsPerWorkgroupSplit = 28 * 1024;
 
 template <typename DT, int D, int G>
 nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
   dim3 grid(a.num_kv_heads, batch, a.max_chunks);
   const dim3 block(64 * kDecodeWaves);
-  static_assert(decode_static_lds<D, G, kDecodeWaves>() < kDecodeLdsPerWorkgroup, "LDS");
-  const size_t pad = kDecodeLdsPerWorkgroup - decode_static_lds<D, G, kDecodeWaves>();
+  static_assert(decode_static_lds<D, G, kDecodeWaves>() < kDecodeLdsPerWorkgroupSplit, "LDS");
+  const size_t pad = (a.max_chunks > 1 ? kDecodeLdsPerWorkgroupSplit : kDecodeLdsPerWorkgroup) -
+                     decode_static_lds<D, G, kDecodeWaves>();
   const bool fast = a.bs_shift >= 0 && (1 << a.bs_shift) >= decode_tokens_per_wave_pass<DT, D>();
   if (a.new_slots) {
     if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, true><<<grid, block, pad, s>>>(a);

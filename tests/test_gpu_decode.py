@@ -287,6 +287,35 @@ def test_fused_store_decode_edges(dtype, d, hq, hkv, bs):
     assert_close(got, want, TOL[dtype], "fused edges")
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv,bs", [("bf16", 128, 16, 8, 16), ("f32", 64, 2, 1, 256)])
+def test_fused_store_skipped_slots(dtype, d, hq, hkv, bs):
+    """slot_mapping[b] = -1 in the fused call: nothing is written for b and its decoded
+    token is read from the cache, where the caller stored it beforehand.  Pool bits equal
+    the separate store + decode's; outputs agree within the tolerance."""
+    from paged_kv_cache_319_amd import nv_store_kvcache, nv_paged_decode_store
+    from paged_kv_cache_319_amd.harness import DeviceDecode, to_host_bits, to_host_f64
+    banner(f"fused store with skipped slots {dtype} d{d} bs{bs}")
+    nb = sum(-(-L // bs) for L in EDGE_LENGTHS) + 3
+    sh = Shape(dtype, hq, hkv, d, bs, nb, 0.5 if dtype == "bf16" else 1.0)
+    case = build_decode("skip", sh, EDGE_LENGTHS, seed=hq + d + bs + 5)
+    a, b = DeviceDecode(case), DeviceDecode(case)
+    want = to_host_f64(a.step(0))
+    st = b.steps[0]
+    skip = torch.arange(0, len(EDGE_LENGTHS), 3, device="cuda")
+    nv_store_kvcache(st["k"][skip].contiguous(), st["v"][skip].contiguous(), b.kc, b.vc,
+                     st["slots"][skip].contiguous())
+    slots = st["slots"].clone()
+    slots[skip] = -1
+    out = torch.empty_like(b.out)
+    nv_paged_decode_store(out, st["q"], st["k"], st["v"], slots, b.kc, b.vc, st["tables"],
+                          st["lens"], st["max_len"], case.shape.scale, workspace=b.workspace,
+                          schedule=st["schedule"])
+    torch.cuda.synchronize()
+    assert_close(to_host_f64(out), want, TOL[dtype], "fused with skipped slots")
+    for x, y in ((a.kc, b.kc), (a.vc, b.vc)):
+        assert np.array_equal(to_host_bits(x).view(np.uint8), to_host_bits(y).view(np.uint8))
+
+
 def test_graph_replay_matches_eager():
     """Fused store + decode steps captured as HIP graphs: every replay, interleaved with
     eager work and synchronisations, reproduces the eager outputs and pool bits."""

@@ -396,29 +396,39 @@ template <int D, int G, int NW>
 constexpr size_t decode_static_lds() {
   return sizeof(float) * (2 * NW * G + NW * G * kWave + NW * G * D);
 }
-// LDS reserved per workgroup, which caps how many share a CU: 36 KB (four) when every
-// sequence is one work item, 28 KB (five) when the plan splits sequences into chunks
-// (shorter items, whose start and end latencies more resident workgroups hide).
+// Workgroup shape by plan.  Every sequence one work item: 4 waves, 36 KB of LDS
+// reserved per workgroup (at most four per CU; fewer concurrent streams read the
+// head-strided rows of whole sequences best).  Sequences split into chunks: 8 waves per
+// workgroup (each chunk finishes in half the time, which evens out the few items per
+// resident workgroup such plans have), 56 KB reserved (two per CU, the same 16 waves).
 constexpr size_t kDecodeLdsPerWorkgroup = 36 * 1024;
-constexpr size_t kDecodeLdsPerWorkgroupSplit = 28 * 1024;
+constexpr int kDecodeWavesSplit = 8;
+constexpr size_t kDecodeLdsPerWorkgroupSplit = 56 * 1024;
+
+template <typename DT, int D, int G, int NW, size_t LDS_CAP>
+void launch_decode_kernel(const DecodeArgs& a, int batch, hipStream_t s) {
+  static_assert(decode_static_lds<D, G, NW>() <= LDS_CAP, "LDS");
+  const dim3 grid(a.num_kv_heads, batch, a.max_chunks);
+  const dim3 block(64 * NW);
+  const size_t pad = LDS_CAP - decode_static_lds<D, G, NW>();
+  const bool fast = a.bs_shift >= 0 && (1 << a.bs_shift) >= decode_tokens_per_wave_pass<DT, D>();
+  if (a.new_slots) {
+    if (fast) paged_decode_kernel<DT, D, G, NW, true, true><<<grid, block, pad, s>>>(a);
+    else paged_decode_kernel<DT, D, G, NW, false, true><<<grid, block, pad, s>>>(a);
+  } else {
+    if (fast) paged_decode_kernel<DT, D, G, NW, true, false><<<grid, block, pad, s>>>(a);
+    else paged_decode_kernel<DT, D, G, NW, false, false><<<grid, block, pad, s>>>(a);
+  }
+}
 
 template <typename DT, int D, int G>
 nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
-  dim3 grid(a.num_kv_heads, batch, a.max_chunks);
-  const dim3 block(64 * kDecodeWaves);
-  static_assert(decode_static_lds<D, G, kDecodeWaves>() < kDecodeLdsPerWorkgroupSplit, "LDS");
-  const size_t pad = (a.max_chunks > 1 ? kDecodeLdsPerWorkgroupSplit : kDecodeLdsPerWorkgroup) -
-                     decode_static_lds<D, G, kDecodeWaves>();
-  const bool fast = a.bs_shift >= 0 && (1 << a.bs_shift) >= decode_tokens_per_wave_pass<DT, D>();
-  if (a.new_slots) {
-    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, true><<<grid, block, pad, s>>>(a);
-    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, true><<<grid, block, pad, s>>>(a);
-  } else {
-    if (fast) paged_decode_kernel<DT, D, G, kDecodeWaves, true, false><<<grid, block, pad, s>>>(a);
-    else paged_decode_kernel<DT, D, G, kDecodeWaves, false, false><<<grid, block, pad, s>>>(a);
-  }
-  if (a.max_chunks > 1)
+  if (a.max_chunks > 1) {
+    launch_decode_kernel<DT, D, G, kDecodeWavesSplit, kDecodeLdsPerWorkgroupSplit>(a, batch, s);
     decode_merge_kernel<DT, D><<<dim3(a.num_q_heads, batch), dim3(D), 0, s>>>(a);
+  } else {
+    launch_decode_kernel<DT, D, G, kDecodeWaves, kDecodeLdsPerWorkgroup>(a, batch, s);
+  }
   return nvp_host::launch_status();
 }
 

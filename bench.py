@@ -236,7 +236,9 @@ def extra_block_size(bs, torch):
     case = decode_config("C3", block_size=bs)
     dev = DeviceDecode(case, poison=False)
     nst = len(case.steps)
-    alg = np.array([decode_bytes(st, case.shape)[0] for st in case.steps])
+    sh = case.shape
+    store_bytes = 2 * 2 * case.batch * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * case.batch
+    alg = np.array([decode_bytes(st, sh)[0] for st in case.steps]) + store_bytes
     for t in range(nst):
         dev.step_fused(t)
     state = {"t": 0}
@@ -423,7 +425,8 @@ def cpu_baseline(case, budget_s=12.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build targets one GPU; --gpus must be 1",
+        print(json.dumps({"error": "nvpaged runs on one GPU (sharding across GPUs is a "
+                                   "design note only); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     import torch

@@ -229,11 +229,13 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   constexpr int NKS = BN / 16;           // 16-key contraction slices per tile
   constexpr int KROW = D + EPC;          // padded K row (elements)
   // bf16: V is kept row-major in LDS and read transposed (ds_read_b64_tr_b16); its rows
-  // are padded to 16 elements past head_dim so that the 16 lanes of one transposed read
-  // (4 rows x 32 bytes) fall in distinct banks.  fp32: V is transposed on the way into
-  // LDS, rows of BN + 4 keys.
+  // are padded to 32 elements past head_dim.  The LDS serves 32 lanes of such a read at
+  // once over 64 banks of 4 bytes; those lanes cover 4 rows x 64 bytes, and a row stride
+  // of 16 (mod 64) banks puts the four rows in disjoint banks (the hardware's bank-
+  // conflict counter reads 0; 16 elements of padding gave a 2-way conflict).  fp32: V is
+  // transposed on the way into LDS, rows of BN + 4 keys.
   constexpr bool TRV = DT::kBytes == 2;
-  constexpr int VROW = TRV ? D + 16 : BN + 4;
+  constexpr int VROW = TRV ? D + 32 : BN + 4;
   constexpr int VBUF = TRV ? BN * VROW : D * VROW;
   constexpr int UNITS = (BN / 4) * CPR;  // 4-key x 16-byte staging units per tile
   constexpr int NT = 64 * GW * PB;       // threads per workgroup

@@ -489,7 +489,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": res["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["gbs"] / HBM_PEAK_GBS,
                      "traffic": recorded_traffic(),
-                     "kernel": "paged_decode_kernel<BF16,128,2,4,fast,store>"},
+                     "kernel": "paged_decode_kernel<BF16,128,2,4,fast,store,2>"},
         "cpu_baseline": cpu,
         "extra": extra,
     }

@@ -100,8 +100,11 @@ __device__ __forceinline__ int in_vgpr(int x) {
   return x;
 }
 
-template <typename DT, int D, int G, int NW, bool FAST, bool STORE>
-__global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
+// One workgroup = HPW KV heads (blockIdx.x * HPW ..) of one (sequence, chunk) item, NW
+// waves per head splitting the item's tokens; the heads' waves share nothing but the
+// workgroup, so its rows of consecutive heads are read side by side.
+template <typename DT, int D, int G, int NW, bool FAST, bool STORE, int HPW>
+__global__ __launch_bounds__(64 * NW * HPW) void paged_decode_kernel(DecodeArgs a) {
   using T = typename DT::T;
   constexpr int EPL = DT::kPerLoad;  // elements per 16-byte lane load
   constexpr int LPT = D / EPL;       // lanes per token row
@@ -112,17 +115,18 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
   constexpr int PASS = TPW * NW;
   static_assert(ITERS % 4 == 0 && kWave % TPW == 0, "weights are read four at a time");
 
-  __shared__ float sm_m[NW][G];
-  __shared__ float sm_sum[NW][G];
-  __shared__ __attribute__((aligned(16))) float sm_p[NW][G][kWave];
-  __shared__ float sm_o[NW][G][D];
+  __shared__ float sm_m[NW * HPW][G];
+  __shared__ float sm_sum[NW * HPW][G];
+  __shared__ __attribute__((aligned(16))) float sm_p[NW * HPW][G][kWave];
+  __shared__ float sm_o[NW * HPW][G][D];
 
-  const int j = blockIdx.x;
+  const int wave_all = wave_id();              // 0 .. NW * HPW - 1
+  const int j = blockIdx.x * HPW + wave_all / NW;  // this wave's KV head
   const int b = a.schedule ? a.schedule[blockIdx.y] : static_cast<int>(blockIdx.y);
   const int c = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = wave_id();
+  const int wave = wave_all % NW;              // index among the head's waves
   const int row = lane / LPT;
   const int col = lane % LPT;
 
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_use);
       m_run[h] = m_use;
       const float p = valid ? __builtin_amdgcn_exp2f(s[h] - m_use) : 0.f;
-      sm_p[wave][h][lane] = p;
+      sm_p[wave_all][h][lane] = p;
       l_run[h] = l_run[h] * alpha + p;
       if (alpha != 1.f) {  // wave-uniform
 #pragma unroll
@@ -244,7 +248,7 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
       f32x4 pw[G];
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        pw[h] = *reinterpret_cast<const f32x4*>(&sm_p[wave][h][row * LPT + i]);
+        pw[h] = *reinterpret_cast<const f32x4*>(&sm_p[wave_all][h][row * LPT + i]);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         float vv[EPL];
@@ -296,30 +300,32 @@ __global__ __launch_bounds__(64 * NW) void paged_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_o[wave][h][col * EPL + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) sm_o[wave_all][h][col * EPL + e] = acc[h][e];
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      sm_sum[wave][h] = lsum[h];
-      sm_m[wave][h] = m_run[h];
+      sm_sum[wave_all][h] = lsum[h];
+      sm_m[wave_all][h] = m_run[h];
     }
   }
   __syncthreads();
 
   T* __restrict__ outp = static_cast<T*>(a.out);
-  const int64_t qrow0 = static_cast<int64_t>(b) * a.num_q_heads + qhead0;
-  for (int idx = tid; idx < G * D; idx += 64 * NW) {
-    const int h = idx / D, d = idx % D;
-    float M = sm_m[0][h];
+  for (int idx = tid; idx < HPW * G * D; idx += 64 * NW * HPW) {
+    const int hs = idx / (G * D), h = (idx / D) % G, d = idx % D;
+    const int64_t qrow0 =
+        static_cast<int64_t>(b) * a.num_q_heads + (blockIdx.x * HPW + hs) * G;
+    const int w0 = hs * NW;                    // the waves of KV head blockIdx.x*HPW + hs
+    float M = sm_m[w0][h];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w0 + w][h]);
     float o = 0.f, l = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm_m[w][h] - M);
-      o = fmaf(f, sm_o[w][h][d], o);
-      l = fmaf(f, sm_sum[w][h], l);
+      const float f = __builtin_amdgcn_exp2f(sm_m[w0 + w][h] - M);
+      o = fmaf(f, sm_o[w0 + w][h][d], o);
+      l = fmaf(f, sm_sum[w0 + w][h], l);
     }
     if (nchunks == 1) {
       store_out<DT>(outp + (qrow0 + h) * D + d, o / l);
@@ -387,47 +393,49 @@ Plan make_plan(int batch, int hq, int hkv, int d, int max_context_len) {
   return p;
 }
 
-// Shared memory of one decode workgroup (the kernel's arrays), and the total reserved
-// per workgroup: at most four workgroups (16 waves) share a CU's 160 KB.  Fewer
-// concurrent streams per CU read the head-strided K/V rows faster than the six
-// workgroups the registers would allow (measured on the batch-256, batch-64 and 32K
-// workloads: 2-8 % shorter decode).
+// Shared memory of the arrays of one KV head's NW waves in a decode workgroup.
 template <int D, int G, int NW>
 constexpr size_t decode_static_lds() {
   return sizeof(float) * (2 * NW * G + NW * G * kWave + NW * G * D);
 }
-// Workgroup shape by plan.  Every sequence one work item: 4 waves, 36 KB of LDS
-// reserved per workgroup (at most four per CU; fewer concurrent streams read the
-// head-strided rows of whole sequences best).  Sequences split into chunks: 8 waves per
-// workgroup (each chunk finishes in half the time, which evens out the few items per
-// resident workgroup such plans have), 56 KB reserved (two per CU, the same 16 waves).
+// Workgroup shape by plan (measured on the batch-256, batch-64 and 32K-context
+// workloads).  Every sequence one work item: two KV heads per workgroup, 4 waves per
+// head, 72 KB of LDS reserved (two workgroups, 16 waves per CU; fewer concurrent streams
+// read the head-strided rows of whole sequences best, and the two heads' rows sit side
+// by side); one head of 4 waves with 36 KB when the KV-head count is odd.  Sequences
+// split into chunks: one head of 8 waves per workgroup (each chunk finishes in half the
+// time, which evens out the few items per resident workgroup such plans have), 56 KB
+// reserved (two per CU, the same 16 waves).
 constexpr size_t kDecodeLdsPerWorkgroup = 36 * 1024;
+constexpr size_t kDecodeLdsPerWorkgroupPair = 72 * 1024;
 constexpr int kDecodeWavesSplit = 8;
 constexpr size_t kDecodeLdsPerWorkgroupSplit = 56 * 1024;
 
-template <typename DT, int D, int G, int NW, size_t LDS_CAP>
+template <typename DT, int D, int G, int NW, int HPW, size_t LDS_CAP>
 void launch_decode_kernel(const DecodeArgs& a, int batch, hipStream_t s) {
-  static_assert(decode_static_lds<D, G, NW>() <= LDS_CAP, "LDS");
-  const dim3 grid(a.num_kv_heads, batch, a.max_chunks);
-  const dim3 block(64 * NW);
-  const size_t pad = LDS_CAP - decode_static_lds<D, G, NW>();
+  static_assert(HPW * decode_static_lds<D, G, NW>() <= LDS_CAP, "LDS");
+  const dim3 grid(a.num_kv_heads / HPW, batch, a.max_chunks);
+  const dim3 block(64 * NW * HPW);
+  const size_t pad = LDS_CAP - HPW * decode_static_lds<D, G, NW>();
   const bool fast = a.bs_shift >= 0 && (1 << a.bs_shift) >= decode_tokens_per_wave_pass<DT, D>();
   if (a.new_slots) {
-    if (fast) paged_decode_kernel<DT, D, G, NW, true, true><<<grid, block, pad, s>>>(a);
-    else paged_decode_kernel<DT, D, G, NW, false, true><<<grid, block, pad, s>>>(a);
+    if (fast) paged_decode_kernel<DT, D, G, NW, true, true, HPW><<<grid, block, pad, s>>>(a);
+    else paged_decode_kernel<DT, D, G, NW, false, true, HPW><<<grid, block, pad, s>>>(a);
   } else {
-    if (fast) paged_decode_kernel<DT, D, G, NW, true, false><<<grid, block, pad, s>>>(a);
-    else paged_decode_kernel<DT, D, G, NW, false, false><<<grid, block, pad, s>>>(a);
+    if (fast) paged_decode_kernel<DT, D, G, NW, true, false, HPW><<<grid, block, pad, s>>>(a);
+    else paged_decode_kernel<DT, D, G, NW, false, false, HPW><<<grid, block, pad, s>>>(a);
   }
 }
 
 template <typename DT, int D, int G>
 nv_status launch_decode(const DecodeArgs& a, int batch, hipStream_t s) {
   if (a.max_chunks > 1) {
-    launch_decode_kernel<DT, D, G, kDecodeWavesSplit, kDecodeLdsPerWorkgroupSplit>(a, batch, s);
+    launch_decode_kernel<DT, D, G, kDecodeWavesSplit, 1, kDecodeLdsPerWorkgroupSplit>(a, batch, s);
     decode_merge_kernel<DT, D><<<dim3(a.num_q_heads, batch), dim3(D), 0, s>>>(a);
+  } else if (a.num_kv_heads % 2 == 0) {
+    launch_decode_kernel<DT, D, G, kDecodeWaves, 2, kDecodeLdsPerWorkgroupPair>(a, batch, s);
   } else {
-    launch_decode_kernel<DT, D, G, kDecodeWaves, kDecodeLdsPerWorkgroup>(a, batch, s);
+    launch_decode_kernel<DT, D, G, kDecodeWaves, 1, kDecodeLdsPerWorkgroup>(a, batch, s);
   }
   return nvp_host::launch_status();
 }

@@ -273,6 +273,31 @@ def test_fused_decode_block_size_variants(bs):
             assert_close(got, orc.run_to(t), TOL["bf16"], f"C3 bs{bs} step {t}")
 
 
+@pytest.mark.parametrize("dtype,d,hq,hkv,batch", [("bf16", 64, 16, 2, 768), ("f32", 128, 8, 4, 400),
+                                                  ("bf16", 128, 8, 1, 1600), ("bf16", 128, 32, 8, 200)])
+def test_decode_whole_sequence_plans(dtype, d, hq, hkv, batch):
+    """Batches with batch x KV heads >= 1536 run every sequence as one work item: two KV
+    heads per workgroup when the KV-head count is even, one otherwise.  Two fused steps
+    and one plain decode against the oracle, for other head dims, group sizes and dtypes
+    than the batch-256 workload's."""
+    from paged_kv_cache_319_amd.harness import DeviceDecode, to_host_f64
+    banner(f"whole-sequence decode {dtype} d{d} hq{hq} hkv{hkv} batch{batch}")
+    rng = np.random.default_rng(hq * 13 + d + batch)
+    lengths = rng.integers(1, 300, endpoint=True, size=batch)
+    bs = 16
+    nb = int(sum(-(-(int(L) + 1) // bs) for L in lengths)) + 4
+    sh = Shape(dtype, hq, hkv, d, bs, nb, 0.5 if dtype == "bf16" else 1.0)
+    case = build_decode("whole", sh, lengths, seed=batch + d, steps=2)
+    dev = DeviceDecode(case)
+    orc = OracleDecode(case)
+    assert dev.steps[0]["schedule"] is not None
+    got0 = to_host_f64(dev.step_fused(0))
+    assert_close(got0, orc.run_to(0), TOL[dtype], "whole-sequence fused step 0")
+    dev.store(1)
+    got1 = to_host_f64(dev.decode(1))
+    assert_close(got1, orc.run_to(1), TOL[dtype], "whole-sequence decode step 1")
+
+
 @pytest.mark.parametrize("dtype,d,hq,hkv,bs", [("bf16", 128, 32, 8, 16), ("f32", 64, 2, 1, 16),
                                                ("bf16", 64, 16, 2, 32)])
 def test_fused_store_decode_edges(dtype, d, hq, hkv, bs):

@@ -11,10 +11,10 @@
 // Work decomposition.  A work item is (KV head j, sequence b, chunk c): tokens
 // [c*chunk, (c+1)*chunk) of sequence b.  The host picks the chunk: whole
 // sequences when batch * kv_heads alone fills the chip, otherwise a length
-// that yields roughly 2048 items.  Sequences are visited in the order of an
-// optional schedule (the host's length-descending order from
-// nv_prepare_decode), so the longest items start first and the short ones fill
-// the tail.  One workgroup of NW waves walks its item in passes of TPW*NW
+// that yields roughly 1024 items (at least two chunks per sequence).
+// Sequences are visited in the order of an optional schedule (the host's
+// length-descending order from nv_prepare_decode), so the longest items start
+// first and the short ones fill the tail.  The NW waves of a KV head walk its item in passes of TPW*NW
 // tokens; every lane issues all of its K and V loads of a pass (4 + 4
 // non-temporal 16-byte loads for bf16, head_dim 128: 16 tokens per wave)
 // before any arithmetic.  Short passes keep the kernel small (~80-100 VGPRs):
@@ -40,6 +40,8 @@
 // a second, small kernel merges them.  (Merging inside the first kernel needs
 // device-scope release/acquire fences per workgroup; on this chip each writes
 // back and invalidates a whole L2 and costs far more than the second launch.)
+#include <algorithm>
+
 #include "common.h"
 
 namespace {
@@ -48,7 +50,8 @@ using namespace nvp;
 
 constexpr int kDecodeWaves = 4;
 constexpr int kPass = 256;                // chunk granularity (a multiple of every pass)
-constexpr int kTargetItems = 2048;        // work items wanted when splitting
+constexpr int kSplitBelowItems = 1536;    // split sequences when fewer (head, sequence) items
+constexpr int kTargetSplitItems = 1024;   // work items aimed at when splitting (>= 2 chunks)
 
 struct DecodeArgs {
   void* out;
@@ -378,7 +381,8 @@ Plan make_plan(int batch, int hq, int hkv, int d, int max_context_len) {
   const int max_len = max_context_len < 1 ? 1 : max_context_len;
   const int64_t items = static_cast<int64_t>(batch) * hkv;
   int64_t per_seq = 1;  // chunks per sequence
-  if (items < (kTargetItems * 3) / 4) per_seq = (kTargetItems + items - 1) / items;
+  if (items < kSplitBelowItems)
+    per_seq = std::max<int64_t>(2, (kTargetSplitItems + items - 1) / items);
   int64_t chunk = (max_len + per_seq - 1) / per_seq;
   chunk = static_cast<int64_t>(round_up(static_cast<size_t>(chunk), kPass));
   p.chunk = static_cast<int>(chunk);

@@ -14,13 +14,14 @@
 // that yields roughly 1024 items (at least two chunks per sequence).
 // Sequences are visited in the order of an optional schedule (the host's
 // length-descending order from nv_prepare_decode), so the longest items start
-// first and the short ones fill the tail.  The NW waves of a KV head walk its item in passes of TPW*NW
-// tokens; every lane issues all of its K and V loads of a pass (4 + 4
-// non-temporal 16-byte loads for bf16, head_dim 128: 16 tokens per wave)
-// before any arithmetic.  Short passes keep the kernel small (~80-100 VGPRs):
-// while one workgroup computes, the others on the CU still have loads in flight
-// (batch-256 step: 64-token passes 92 us, 32-token 89.6 us, 16-token 87.7 us,
-// event-timed).  At most four workgroups share a CU (see launch_decode).
+// first and the short ones fill the tail.  The NW waves of a KV head walk its
+// item in passes of TPW*NW tokens; every lane issues all of its K and V loads of
+// a pass (4 + 4 non-temporal 16-byte loads for bf16, head_dim 128: 16 tokens per
+// wave) before any arithmetic.  Short passes keep the kernel small (~80-100
+// VGPRs): while one wave computes, the others on the CU still have loads in
+// flight (batch-256 step: 64-token passes 92 us, 32-token 89.6 us, 16-token
+// 87.7 us, event-timed).  A workgroup holds one or two KV heads and 16 waves
+// share a CU; the shapes per plan are chosen in launch_decode.
 //
 // Lanes.  A token row of head j (head_dim elements) is spread over LPT lanes of
 // 16 bytes, so one wave-wide load fetches TPL whole rows.  The g query heads of

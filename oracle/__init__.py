@@ -21,6 +21,12 @@ traces, a published XXH64 digest and brute-force invariants over random traces
 (tests/test_block_manager_oracle.py, with planted mistakes in
 tests/test_block_manager_mutants.py).
 
+``oracle.sampler`` restates the walkthrough's section 六 sampler (temperature scaling,
+Gumbel noise added, argmax; temperature 0 is greedy).  It is pinned by the Gumbel-max
+theorem (token frequencies over many noise draws against softmax(logits / T)), a
+pure-Python brute force, the greedy limit, tie and shift rules
+(tests/test_oracle_sampler.py, with planted mistakes in the same file).
+
 Every attention function below is pinned by CPU tests against brute force, closed forms,
 invariants and a library special case (torch's scaled_dot_product_attention in
 float64); none is "parity unpinned".
@@ -29,3 +35,4 @@ from .paged_oracle import (  # noqa: F401
     to_f64, slot_of, decode_slot_mapping, prefill_metadata, fill_slot_mapping,
     store_kvcache, gather, attend, paged_decode, paged_prefill, new_pool,
 )
+from .sampler import sample, first_argmax  # noqa: F401,E402

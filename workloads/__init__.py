@@ -11,5 +11,5 @@ on their own from what is generated here.
 from .gen import (  # noqa: F401
     Shape, Fill, DecodeStep, DecodeCase, PrefillCase,
     CONFIG_NAMES, decode_config, prefill_config, build_decode, build_prefill,
-    bf16_bits_from_f32, poison_bits, np_storage_dtype,
+    bf16_bits_from_f32, poison_bits, np_storage_dtype, SamplerCase, sampler_case,
 )

@@ -375,3 +375,44 @@ def prefill_config(name: str = "C5", *, num_seqs: Optional[int] = None,
     n = len_rng.integers(min(100, max_new), max_new, endpoint=True, size=S)
     p = 256 * len_rng.integers(0, 4, endpoint=True, size=S)
     return build_prefill(name, sh, n, p, seed=seed, pad_to=128, causal=True)
+
+
+# --------------------------------------------------------------------------
+# token sampler workload
+# --------------------------------------------------------------------------
+
+@dataclass
+class SamplerCase:
+    """Logits of one decode step, per-row temperatures and the Gumbel noise the
+    sampler consumes.  ``logits`` is float32 or raw bfloat16 bits (uint16)."""
+    dtype: str
+    logits: np.ndarray        # [batch, vocab]
+    temperatures: np.ndarray  # float32 [batch]; 0 = greedy row
+    gumbel: np.ndarray        # float32 [batch, vocab], standard Gumbel draws
+
+    @property
+    def batch(self) -> int:
+        return int(self.logits.shape[0])
+
+    @property
+    def vocab(self) -> int:
+        return int(self.logits.shape[1])
+
+
+def sampler_case(batch: int = 256, vocab: int = 151936, *, dtype: str = "bf16",
+                 sigma: float = 2.0, greedy_fraction: float = 0.125,
+                 t_range=(0.5, 1.0), seed: int = 2000) -> SamplerCase:
+    """Seeded sampler input.  Defaults: the decode batch of 256 over a Qwen3-sized
+    vocabulary of 151,936 entries; logits N(0, 1) * 2 (rounded to bf16 for bf16);
+    round(batch / 8) rows (seeded choice) at temperature 0, the others U[0.5, 1.0);
+    noise from numpy's Gumbel(0, 1) generator, stored as float32."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, batch, vocab]))
+    logits = _draw(rng, (batch, vocab), sigma, dtype)
+    temps = rng.uniform(t_range[0], t_range[1], size=batch).astype(np.float32)
+    n_greedy = int(round(batch * greedy_fraction))
+    if n_greedy:
+        temps[rng.choice(batch, size=n_greedy, replace=False)] = 0.0
+    gumbel = np.empty((batch, vocab), dtype=np.float32)
+    for b in range(batch):                       # row by row: bounded float64 temporaries
+        gumbel[b] = rng.gumbel(size=vocab)
+    return SamplerCase(dtype, logits, temps, gumbel)

@@ -37,7 +37,7 @@ def parse():
                          "~6 %% slower)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["c3", "c5", "copy"], default=None,
+    ap.add_argument("--only", choices=["c3", "c5", "copy", "sampler"], default=None,
                     help="run one leg only (for profiler runs)")
     return ap.parse_args()
 
@@ -327,6 +327,32 @@ def extra_prefill(torch, reps=20, bs=None):
     return out
 
 
+def sampler_bytes(case):
+    """Algorithmic bytes of one sampler call: every logit, the noise of the rows with
+    T > 0 (greedy rows read none), the temperatures and the tokens."""
+    es = 2 if case.dtype == "bf16" else 4
+    sampled = int(np.count_nonzero(case.temperatures))
+    return case.batch * case.vocab * es + sampled * case.vocab * 4 + 8 * case.batch
+
+
+def extra_sampler(torch, reps=50, dtype="bf16"):
+    """Temperature + Gumbel-max sampler over batch 256 x vocabulary 151,936 (1/8 of the
+    rows greedy), timed after 50 ms of warm launches."""
+    from workloads import sampler_case
+    from paged_kv_cache_319_amd.harness import DeviceSampler
+    case = sampler_case(dtype=dtype)
+    dev = DeviceSampler(case)
+    warm(dev.sample, torch)
+    ms = time_region(dev.sample, reps, torch)
+    b = sampler_bytes(case)
+    tag = "sampler" if dtype == "bf16" else f"sampler_{dtype}"
+    out = {f"{tag}_us": float(ms * 1e3), f"{tag}_gbs": float(b / (ms * 1e-3) / 1e9),
+           f"{tag}_hbm_frac": float(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)}
+    del dev
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(torch, reps=5):
     """A plain 1 GiB device copy: known bytes for scaling the HBM traffic counters."""
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -441,6 +467,9 @@ def main():
     if args.only == "c5":
         print(json.dumps(extra_prefill(torch)), flush=True)
         return
+    if args.only == "sampler":
+        print(json.dumps(extra_sampler(torch)), flush=True)
+        return
     extra = {}
     print(f"[bench] headline workload: {args.warmup} warmup + {args.steps} timed steps",
           file=sys.stderr, flush=True)
@@ -455,6 +484,9 @@ def main():
             print(f"[bench] extra block size {bs}", file=sys.stderr, flush=True)
             extra.update(extra_block_size(bs, torch))
         extra.update(extra_prefill(torch, bs=16))
+        print("[bench] extra sampler", file=sys.stderr, flush=True)
+        extra.update(extra_sampler(torch))
+        extra.update(extra_sampler(torch, dtype="f32"))
         extra.update(extra_block_manager())
     extra.update({k: res[k] for k in ("kernel_us_mean", "per_launch_event_us_p10",
                                       "per_launch_event_us_p50", "per_launch_event_us_p90",

@@ -3,8 +3,9 @@
  *
  * C ABI of the hot path of a nano-vLLM style engine: the store of new K/V rows
  * into a block-paged cache, paged GQA decode attention and packed varlen causal
- * prefill attention that reads cached prefix blocks, plus the host-side metadata
- * builders that produce slot_mapping and cu_seqlens.
+ * prefill attention that reads cached prefix blocks, the temperature + Gumbel-max
+ * token sampler, plus the host-side metadata builders that produce slot_mapping
+ * and cu_seqlens.
  *
  * Sources for the operations (web pages on nano-vLLM):
  *   [walkthrough]  the xingyun3d.csdn.net article on nano-vllm, sections
@@ -188,6 +189,35 @@ nv_status nv_paged_prefill(void* out, const void* q,
 /* Query rows per prefill work tile for this head configuration (0 if unsupported).
  * A tile schedule for nv_paged_prefill is built with this many rows per tile. */
 int32_t nv_paged_prefill_tile_rows(int32_t num_q_heads, int32_t num_kv_heads);
+
+/* ------------------------------------------------------------------------- *
+ * token sampler  ([walkthrough] 六, sampler paragraph: divide the logits by the
+ * temperature, add Gumbel noise, take the argmax; [deep dive] 3.3: temperature 0
+ * is greedy decoding)
+ *
+ * tokens[b] = argmax_i logits[b, i]                         if temperatures[b] == 0
+ *           = argmax_i (logits[b, i] / temperatures[b] + gumbel[b, i])  otherwise,
+ * with the score computed in binary32 (correctly rounded division, then addition)
+ * and ties resolved to the lowest index.  A greedy row never reads its noise row.
+ *   tokens: int32 [batch] device output.
+ *   logits: [batch, vocab] dtype elements (NV_F32 or NV_BF16), row b starting at
+ *     logits + b * logits_row_stride elements.
+ *   temperatures: float [batch] device array; each 0 or positive and finite.
+ *   gumbel: float [batch, vocab] standard Gumbel(0, 1) draws made by the caller,
+ *     row b at gumbel + b * gumbel_row_stride.  Must not be NULL.
+ *   NaN logits or noise are undefined behaviour (the result may be out of range).
+ *   workspace: device scratch of at least nv_sample_workspace_size(batch, vocab)
+ *     bytes (NULL allowed when that size is 0) for per-chunk partial results when
+ *     rows are split over several workgroups; merged by a second kernel on the
+ *     same stream.  No initial contents are required; calls sharing a workspace
+ *     must be ordered on one stream.  batch == 0 is a no-op; batch <= 65535.
+ * ------------------------------------------------------------------------- */
+size_t nv_sample_workspace_size(int32_t batch, int32_t vocab);
+
+nv_status nv_sample(int32_t* tokens, const void* logits, int64_t logits_row_stride,
+                    const float* temperatures, const float* gumbel,
+                    int64_t gumbel_row_stride, int32_t batch, int32_t vocab,
+                    int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
  * Host-side metadata builders ([walkthrough] 七: prepare_decode /

@@ -39,6 +39,11 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
+    "nv_sample_workspace_size": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "nv_sample": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_size_t, ctypes.c_void_p]),
     "nv_paged_prefill_tile_rows": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nv_prepare_decode": (ctypes.c_int, [
         c_i32p, ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -209,6 +209,37 @@ def nv_paged_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     _check("nv_paged_prefill", st)
 
 
+def nv_sample_workspace_size(batch: int, vocab: int) -> int:
+    return int(_native.load().nv_sample_workspace_size(batch, vocab))
+
+
+def nv_sample(tokens: torch.Tensor, logits: torch.Tensor, temperatures: torch.Tensor,
+              gumbel: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> None:
+    """tokens: int32 [B] (device); logits: [B, V] float32 or bfloat16 (rows may be
+    strided); temperatures: float32 [B]; gumbel: float32 [B, V] (rows may be strided).
+    Without ``workspace`` a cached per-device buffer is used."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be [B, V] with contiguous rows")
+    B, V = logits.shape
+    if gumbel.shape != (B, V) or gumbel.stride(1) != 1 or gumbel.dtype != torch.float32:
+        raise ValueError("gumbel must be float32 [B, V] with contiguous rows")
+    if temperatures.dtype != torch.float32 or temperatures.numel() != B:
+        raise ValueError("temperatures must be float32 with one entry per row")
+    if tokens.dtype != torch.int32 or tokens.numel() != B:
+        raise ValueError("tokens must be int32 with one entry per row")
+    need = nv_sample_workspace_size(B, V)
+    if workspace is None:
+        workspace = decode_workspace(logits.device, need)
+    ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _native.load().nv_sample(
+        _dev(tokens, "tokens"), _dev(logits, "logits", False), logits.stride(0),
+        _dev(temperatures, "temperatures"), _dev(gumbel, "gumbel", False), gumbel.stride(0),
+        B, V, _dtype_code(logits), ws_ptr, ws_bytes, _stream(stream, logits.device))
+    _check("nv_sample", st)
+
+
 def nv_paged_prefill_tile_rows(num_q_heads: int, num_kv_heads: int) -> int:
     return int(_native.load().nv_paged_prefill_tile_rows(num_q_heads, num_kv_heads))
 

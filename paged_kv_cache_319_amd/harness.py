@@ -170,3 +170,23 @@ class DevicePrefill:
     def step(self):
         self.store()
         return self.attend()
+
+
+class DeviceSampler:
+    """A sampler workload resident on the device: logits, temperatures, Gumbel noise."""
+
+    def __init__(self, case, device="cuda:0"):
+        from .api import nv_sample_workspace_size
+        self.case = case
+        self.logits = to_device(case.logits, case.dtype, device)
+        self.temps = torch.from_numpy(np.ascontiguousarray(case.temperatures,
+                                                           dtype=np.float32)).to(device)
+        self.gumbel = torch.from_numpy(np.ascontiguousarray(case.gumbel, dtype=np.float32)).to(device)
+        self.tokens = torch.empty(case.batch, dtype=torch.int32, device=device)
+        n = nv_sample_workspace_size(case.batch, case.vocab)
+        self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+    def sample(self):
+        from .api import nv_sample
+        nv_sample(self.tokens, self.logits, self.temps, self.gumbel, workspace=self.ws)
+        return self.tokens

@@ -149,6 +149,20 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.nv_paged_prefill_tile_rows(32, 8) == 64
     assert lib.nv_paged_prefill_tile_rows(8, 8) == 256
     assert lib.nv_paged_prefill_tile_rows(12, 8) == 0
+    # sampler: short stride, bad dtype, null noise, too-small workspace, batch 0
+    V = 151936
+    n = lib.nv_sample_workspace_size(256, V)
+    assert n >= 256 * 8 * 8                                         # split rows: partials
+    assert lib.nv_sample_workspace_size(300, 4096) == 0             # one workgroup per row
+    smp = lambda **kw: [p, p, kw.get("ls", V), p, kw.get("g", p), V, kw.get("B", 256), V,
+                        kw.get("dt", 1), kw.get("ws", p), kw.get("wsn", n), s]
+    assert lib.nv_sample(*smp(ls=V - 1)) == -1
+    assert lib.nv_sample(*smp(dt=2)) == -2
+    assert lib.nv_sample(*smp(g=None)) == -1
+    assert lib.nv_sample(*smp(wsn=n - 1)) == -3
+    assert lib.nv_sample(*smp(ws=None)) == -3
+    assert lib.nv_sample(*smp(B=70000, wsn=1 << 40)) == -2
+    assert lib.nv_sample(*smp(B=0)) == 0
 
 
 def test_prepare_decode_schedule_is_length_descending(lib):

@@ -234,9 +234,11 @@ __global__ __launch_bounds__(kThreads) void sample_merge_kernel(
   if (lane == 0) tokens[row] = best.i;
 }
 
-// Work split: enough workgroups to cover the chip several times over, each
+// Work split: enough workgroups to cover the chip many times over, each
 // streaming at least kMinChunk elements; chunk lengths are multiples of kUnit.
-constexpr int64_t kTargetGroups = 2048;
+// Batch 256 x 151,936 with a flushed cache: 2048 groups 45.3 us, 4096 42.8 us,
+// 8192 (32 chunks of 4752 per row) 41.8 us.
+constexpr int64_t kTargetGroups = 8192;
 constexpr int32_t kMinChunk = 4096;
 
 struct Plan {

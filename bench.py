@@ -210,30 +210,33 @@ def warm(fn, torch, seconds=0.05):
         torch.cuda.synchronize()
 
 
-def extra_decode(name, torch, reps=50):
-    """Decode alone on a fresh pool, timed after 50 ms of warm launches."""
+def extra_decode(name, torch, reps=50, tp=1):
+    """Decode alone on a fresh pool, timed after 50 ms of warm launches.  ``tp`` > 1 runs
+    one GPU's head shard of the workload (heads / tp, same lengths and tables)."""
     from workloads import decode_config
     from paged_kv_cache_319_amd.harness import DeviceDecode
-    case = decode_config(name)
+    case = decode_config(name, tp=tp)
     dev = DeviceDecode(case, poison=True)
     b, _ = decode_bytes(case.steps[0], case.shape)
     dev.store(0)
     warm(lambda: dev.decode(0), torch)
     ms = time_region(lambda: dev.decode(0), reps, torch)
-    out = {f"{name.lower()}_decode_us": float(ms * 1e3),
-           f"{name.lower()}_decode_gbs": float(b / (ms * 1e-3) / 1e9)}
+    tag = name.lower() if tp == 1 else f"{name.lower()}_tp{tp}_shard"
+    out = {f"{tag}_decode_us": float(ms * 1e3),
+           f"{tag}_decode_gbs": float(b / (ms * 1e-3) / 1e9)}
     del dev
     torch.cuda.empty_cache()
     return out
 
 
-def extra_block_size(bs, torch):
+def extra_block_size(bs, torch, tp=1):
     """The batch-256 workload redrawn with block size `bs` (same lengths, pool bytes and
-    shared 256-token prefixes): fused store + decode cycling over the 50 steps for 50 ms
-    untimed, then one timed pass from step 0, back to back."""
+    shared 256-token prefixes), or as one GPU's head shard under `tp`-way head
+    parallelism: fused store + decode cycling over the 50 steps for 50 ms untimed, then
+    one timed pass from step 0, back to back."""
     from workloads import decode_config
     from paged_kv_cache_319_amd.harness import DeviceDecode
-    case = decode_config("C3", block_size=bs)
+    case = decode_config("C3", block_size=bs, tp=tp)
     dev = DeviceDecode(case, poison=False)
     nst = len(case.steps)
     sh = case.shape
@@ -249,8 +252,9 @@ def extra_block_size(bs, torch):
     warm(one, torch)
     state["t"] = 0
     ms = time_region(one, nst, torch)
-    out = {f"c3_bs{bs}_fused_us": float(ms * 1e3),
-           f"c3_bs{bs}_fused_gbs": float(alg.mean() / (ms * 1e-3) / 1e9)}
+    tag = f"c3_bs{bs}" if tp == 1 else f"c3_tp{tp}_shard"
+    out = {f"{tag}_fused_us": float(ms * 1e3),
+           f"{tag}_fused_gbs": float(alg.mean() / (ms * 1e-3) / 1e9)}
     del dev
     torch.cuda.empty_cache()
     return out
@@ -503,6 +507,9 @@ def main():
             print(f"[bench] extra block size {bs}", file=sys.stderr, flush=True)
             extra.update(extra_block_size(bs, torch))
         extra.update(extra_prefill(torch, bs=16))
+        print("[bench] extra head shards", file=sys.stderr, flush=True)
+        extra.update(extra_block_size(None, torch, tp=2))
+        extra.update(extra_decode("C4", torch, tp=2))
         print("[bench] extra sampler", file=sys.stderr, flush=True)
         extra.update(extra_sampler(torch))
         extra.update(extra_sampler(torch, dtype="f32"))

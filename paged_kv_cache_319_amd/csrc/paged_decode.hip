@@ -52,7 +52,7 @@ using namespace nvp;
 constexpr int kDecodeWaves = 4;
 constexpr int kPass = 256;                // chunk granularity (a multiple of every pass)
 constexpr int kSplitBelowItems = 1536;    // split sequences when fewer (head, sequence) items
-constexpr int kTargetSplitItems = 1024;   // work items aimed at when splitting (>= 2 chunks)
+constexpr int kTargetSplitItems = 512;    // work items aimed at when splitting (>= 2 chunks)
 
 struct DecodeArgs {
   void* out;

@@ -319,15 +319,24 @@ SHAPES = {
 
 def decode_config(name: str, *, batch: Optional[int] = None, steps: Optional[int] = None,
                   num_blocks: Optional[int] = None, seed: Optional[int] = None,
-                  block_size: Optional[int] = None) -> DecodeCase:
+                  block_size: Optional[int] = None, tp: int = 1) -> DecodeCase:
     """C1-C4.  ``batch``/``steps``/``num_blocks`` shrink a workload for CPU-sized tests
     (same recipe, smaller draw); the defaults are the full workloads.
 
     ``block_size`` redraws the workload with another block size: the same lengths and
     pool bytes (``num_blocks`` scaled by the size ratio unless given), and C3's shared
-    prefixes cover the same 1-2 x 256 tokens (as whole blocks of the new size)."""
+    prefixes cover the same 1-2 x 256 tokens (as whole blocks of the new size).
+
+    ``tp`` gives one GPU's share of the workload under head-parallel sharding over ``tp``
+    GPUs: num_q_heads / tp query heads and num_kv_heads / tp KV heads, the same lengths,
+    block tables and sharing (each GPU holds its heads' slice of every block)."""
     idx = CONFIG_NAMES.index(name)
     sh = SHAPES[name]
+    if tp < 1 or sh.num_kv_heads % tp:
+        raise ValueError(f"{name} has {sh.num_kv_heads} KV heads: cannot shard over {tp}")
+    if tp > 1:
+        sh = Shape(sh.dtype, sh.num_q_heads // tp, sh.num_kv_heads // tp, sh.head_dim,
+                   sh.block_size, sh.num_blocks, sh.sigma)
     bs = sh.block_size if block_size is None else int(block_size)
     if bs < 1 or (sh.block_size * sh.num_blocks) % bs:
         raise ValueError(f"block size {bs} does not divide the {name} pool")

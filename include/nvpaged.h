@@ -206,11 +206,12 @@ int32_t nv_paged_prefill_tile_rows(int32_t num_q_heads, int32_t num_kv_heads);
  *   gumbel: float [batch, vocab] standard Gumbel(0, 1) draws made by the caller,
  *     row b at gumbel + b * gumbel_row_stride.  Must not be NULL.
  *   NaN logits or noise are undefined behaviour (the result may be out of range).
- *   workspace: device scratch of at least nv_sample_workspace_size(batch, vocab)
- *     bytes (NULL allowed when that size is 0) for per-chunk partial results when
- *     rows are split over several workgroups; merged by a second kernel on the
- *     same stream.  No initial contents are required; calls sharing a workspace
- *     must be ordered on one stream.  batch == 0 is a no-op; batch <= 65535.
+ *   workspace: 4-byte aligned device scratch of at least
+ *     nv_sample_workspace_size(batch, vocab) bytes (NULL allowed when that size
+ *     is 0) for per-chunk partial results when rows are split over several
+ *     workgroups; merged by a second kernel on the same stream.  No initial
+ *     contents are required; calls sharing a workspace must be ordered on one
+ *     stream.  batch == 0 is a no-op; batch <= 65535.
  * ------------------------------------------------------------------------- */
 size_t nv_sample_workspace_size(int32_t batch, int32_t vocab);
 

@@ -202,7 +202,8 @@ __global__ __launch_bounds__(kThreads) void sample_partial_kernel(
   const int32_t row = blockIdx.y;
   const int32_t c = blockIdx.x;
   const int32_t lo = c * chunk;
-  const int32_t hi = min(vocab, lo + chunk);
+  const int32_t hi = static_cast<int32_t>(
+      min(static_cast<int64_t>(vocab), static_cast<int64_t>(lo) + chunk));
   const float t = temperatures[row];
   const typename DT::T* zr = logits + static_cast<int64_t>(row) * logits_stride;
   const float* gr = gumbel + static_cast<int64_t>(row) * gumbel_stride;
@@ -292,6 +293,7 @@ extern "C" nv_status nv_sample(int32_t* tokens, const void* logits, int64_t logi
   const Plan p = plan_for(batch, vocab);
   const size_t need = nv_sample_workspace_size(batch, vocab);
   if (workspace_bytes < need || (need > 0 && !workspace)) return NV_ERR_WORKSPACE_TOO_SMALL;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3)) return NV_ERR_INVALID_ARG;
   float* ps = nullptr;
   int32_t* pi = nullptr;
   if (need > 0) {

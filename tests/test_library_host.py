@@ -162,6 +162,7 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.nv_sample(*smp(wsn=n - 1)) == -3
     assert lib.nv_sample(*smp(ws=None)) == -3
     assert lib.nv_sample(*smp(B=70000, wsn=1 << 40)) == -2
+    assert lib.nv_sample(*smp(ws=ctypes.c_void_p(18))) == -1         # misaligned workspace
     assert lib.nv_sample(*smp(B=0)) == 0
 
 

@@ -156,3 +156,48 @@ def test_prefill_negative_and_zero_scale(dtype, scale):
                      dev.tables, scale, True, tile_schedule=dev.tiles)
     want = oracle_prefill(case, scale=scale)[0]
     assert_close(to_host_f64(out), want, TOL[dtype], f"prefill scale {scale}")
+
+
+def test_prefill_long_sequence_sampled_rows():
+    """A 4096-token prompt after a 4096-token cached prefix (8192 keys, the 32 query /
+    8 KV heads of the batch workload), next to a one-token and a prefix-free sequence:
+    the store bit-exact over the whole pool, attention against the oracle on sampled
+    rows of the long sequence (tile edges, the first and the last row) and on every row
+    of the short ones."""
+    import oracle
+    from oracle_runs import oracle_pools
+    from paged_kv_cache_319_amd.harness import DevicePrefill, to_host_f64, to_host_bits
+    banner("prefill long sequence, sampled rows")
+    new, cached = [4096, 1, 777], [4096, 512, 0]
+    sh = Shape("bf16", 32, 8, 128, 256, sum(-(-(n + p) // 256) for n, p in zip(new, cached)) + 2,
+               0.5)
+    case = build_prefill("long", sh, new, cached, seed=21, pad_to=128)
+    dev = DevicePrefill(case)
+    dev.store()
+    got = to_host_f64(dev.attend())
+    torch.cuda.synchronize()
+
+    kc, vc = oracle_pools(sh, case.fill)
+    cu_q, cu_k, _, _, slots = oracle.prefill_metadata(case.block_tables, case.num_cached,
+                                                      case.num_new, sh.block_size, case.pad_to)
+    oracle.store_kvcache(kc, vc, case.k_new, case.v_new, slots)
+    for x, y in ((dev.kc, kc), (dev.vc, vc)):
+        assert np.array_equal(to_host_bits(x).view(np.uint8), y.view(np.uint8))
+
+    q64 = oracle.to_f64(case.q)
+    g = sh.num_q_heads // sh.num_kv_heads
+    rng = np.random.default_rng(5)
+    for s in range(len(new)):
+        n, k = new[s], new[s] + cached[s]
+        q0 = int(cu_q[s])
+        if n > 1000:
+            rows = np.unique(np.concatenate([[0, 31, 32, 63, 64, 65, n - 65, n - 64, n - 1],
+                                             rng.choice(n, 40, replace=False)]))
+        else:
+            rows = np.arange(n)
+        K = oracle.gather(kc, case.block_tables[s], k)
+        V = oracle.gather(vc, case.block_tables[s], k)
+        last = (k - n) + rows
+        for h in range(sh.num_q_heads):
+            want = oracle.attend(q64[q0 + rows, h], K[:, h // g], V[:, h // g], sh.scale, last)
+            assert_close(got[q0 + rows, h], want, TOL["bf16"], f"long prefill seq {s} head {h}")

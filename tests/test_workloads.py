@@ -82,3 +82,27 @@ def test_seeded_determinism():
 def test_pool_exhaustion_raises():
     with pytest.raises(MemoryError):
         build_decode("t", Shape("f32", 1, 1, 4, 4, 3, 1.0), [5, 9], seed=1)
+
+
+@pytest.mark.parametrize("name,tp", [("C3", 2), ("C3", 4), ("C4", 2), ("C2", 8)])
+def test_head_shard_keeps_structure(name, tp):
+    """One GPU's head shard: num_q_heads / tp and num_kv_heads / tp, with the lengths,
+    block tables and shared blocks of the unsharded workload."""
+    kw = {"batch": 12, "num_blocks": 300, "steps": 3} if name == "C3" else \
+         {"batch": 2, "num_blocks": 300} if name == "C4" else {"batch": 12, "num_blocks": 300}
+    full = decode_config(name, **kw)
+    shard = decode_config(name, tp=tp, **kw)
+    assert shard.shape.num_q_heads * tp == full.shape.num_q_heads
+    assert shard.shape.num_kv_heads * tp == full.shape.num_kv_heads
+    assert shard.shape.num_q_heads // shard.shape.num_kv_heads == full.shape.group
+    for a, b in zip(full.steps, shard.steps):
+        assert np.array_equal(a.context_lens, b.context_lens)
+        assert np.array_equal(a.block_tables, b.block_tables)
+        assert b.q.shape[1] == shard.shape.num_q_heads and b.k_new.shape[1] == shard.shape.num_kv_heads
+
+
+def test_head_shard_rejects_uneven_split():
+    with pytest.raises(ValueError):
+        decode_config("C1", tp=2)       # one KV head
+    with pytest.raises(ValueError):
+        decode_config("C3", tp=3, batch=4, steps=1)

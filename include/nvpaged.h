@@ -40,7 +40,7 @@
  *     are reported before anything is enqueued; a failed launch returns
  *     NV_ERR_HIP.  Values inside device arrays (slots, block ids, lengths) are
  *     preconditions and are not checked: out-of-range values are undefined
- *     behaviour.
+ *     behaviour, unless check mode is on (nv_set_check_mode below).
  */
 #ifndef NVPAGED_H
 #define NVPAGED_H
@@ -219,6 +219,33 @@ nv_status nv_sample(int32_t* tokens, const void* logits, int64_t logits_row_stri
                     const float* temperatures, const float* gumbel,
                     int64_t gumbel_row_stride, int32_t batch, int32_t vocab,
                     int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------- *
+ * Check mode.  When on, every GPU entry point above first validates the
+ * preconditions on its device arrays with validation kernels on its stream,
+ * waits for them (a host synchronisation), and returns NV_ERR_INVALID_ARG
+ * without launching its own work if one fails: slots in range and unique
+ * (-1 allowed), context lengths within [1, max_context_len] and the table
+ * width, block ids of used blocks within [0, num_blocks), a decode schedule that
+ * is a permutation, fused-store slots equal to the slot of position
+ * context_lens[b] - 1 (or -1), cu_seqlens starting at 0 and non-decreasing
+ * with at least as many keys as queries per sequence and within max_seqlen_q/k,
+ * a tile schedule listing each existing tile once, sampler temperatures finite
+ * and >= 0.  (Uniqueness is checked for arrays of up to 65536 entries; whether
+ * a slot lands in a block that several sequences share is not checked.)  Check
+ * mode is for debugging: it costs a synchronisation per call and must not be
+ * used under stream capture.  It starts on when the environment variable
+ * NV_CHECK is set to anything but "0" at the first call, off otherwise.
+ * ------------------------------------------------------------------------- */
+
+/* Turns check mode on (non-zero) or off; returns the previous setting (0 / 1). */
+int32_t nv_set_check_mode(int32_t enabled);
+
+/* Description of a violation found by the calling thread's latest check (the
+ * lowest-numbered kind found, at its lowest element index; "no violation" if
+ * it passed).  Static storage, valid until the
+ * thread's next checked call. */
+const char* nv_check_message(void);
 
 /* ------------------------------------------------------------------------- *
  * Host-side metadata builders ([walkthrough] 七: prepare_decode /

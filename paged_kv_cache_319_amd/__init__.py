@@ -10,7 +10,7 @@ from .api import (  # noqa: F401
     nv_status_string, nv_store_kvcache, nv_paged_decode_workspace_size, nv_paged_decode,
     nv_paged_decode_store,
     nv_paged_prefill, nv_paged_prefill_tile_rows, nv_prepare_decode, nv_prepare_prefill,
-    decode_workspace, nv_sample_workspace_size, nv_sample,
+    decode_workspace, nv_sample_workspace_size, nv_sample, nv_set_check_mode, nv_check_message,
 )
 from .blocks import BlockManager, nv_bm_xxh64  # noqa: F401
 from ._native import LIB_PATH, load as load_library  # noqa: F401

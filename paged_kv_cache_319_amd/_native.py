@@ -44,6 +44,8 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_size_t, ctypes.c_void_p]),
+    "nv_set_check_mode": (ctypes.c_int32, [ctypes.c_int32]),
+    "nv_check_message": (ctypes.c_char_p, []),
     "nv_paged_prefill_tile_rows": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32]),
     "nv_prepare_decode": (ctypes.c_int, [
         c_i32p, ctypes.c_int32, c_i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -209,6 +209,16 @@ def nv_paged_prefill(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     _check("nv_paged_prefill", st)
 
 
+def nv_set_check_mode(enabled: bool) -> bool:
+    """Turn check mode (device-data precondition validation before each launch) on or
+    off; returns the previous setting."""
+    return bool(_native.load().nv_set_check_mode(1 if enabled else 0))
+
+
+def nv_check_message() -> str:
+    return _native.load().nv_check_message().decode()
+
+
 def nv_sample_workspace_size(batch: int, vocab: int) -> int:
     return int(_native.load().nv_sample_workspace_size(batch, vocab))
 

@@ -161,3 +161,18 @@ inline nv_status launch_status() {
 inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 }  // namespace nvp_host
+
+// Check mode (check.hip): validation of the device-data preconditions before a launch.
+namespace nvp_check {
+bool on();
+nv_status store(const int32_t* slots, int32_t n, int32_t num_blocks, int32_t block_size,
+                void* stream);
+nv_status decode(const int32_t* tables, int32_t width, const int32_t* lens,
+                 const int32_t* schedule, const int32_t* new_slots, int32_t batch,
+                 int32_t block_size, int32_t num_blocks, int32_t max_len, void* stream);
+nv_status prefill(const int32_t* cu_q, const int32_t* cu_k, const int32_t* tables, int32_t width,
+                  int32_t num_seqs, int32_t block_size, int32_t num_blocks, int32_t max_q,
+                  int32_t max_k, const int32_t* tiles, int32_t num_tiles, int32_t tile_rows,
+                  void* stream);
+nv_status sample(const float* temperatures, int32_t batch, void* stream);
+}  // namespace nvp_check

@@ -509,6 +509,12 @@ nv_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   const Plan p = make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_context_len);
   if (p.max_chunks > 65535) return NV_ERR_UNSUPPORTED;
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return NV_ERR_WORKSPACE_TOO_SMALL;
+  if (nvp_check::on()) {
+    const nv_status st = nvp_check::decode(block_tables, max_blocks_per_seq, context_lens, schedule,
+                                           new_slots, batch, block_size, num_blocks,
+                                           max_context_len, stream);
+    if (st != NV_OK) return st;
+  }
 
   DecodeArgs a{};
   a.out = out;

@@ -696,6 +696,13 @@ extern "C" nv_status nv_paged_prefill(void* out, const void* q, const void* k_ca
   if (num_seqs > 65535 || static_cast<int64_t>(num_kv_heads) * g > 65535 || num_tiles > 65535)
     return NV_ERR_UNSUPPORTED;
 
+  if (nvp_check::on()) {
+    const nv_status st = nvp_check::prefill(
+        cu_seqlens_q, cu_seqlens_k, block_tables, max_blocks_per_seq, num_seqs, block_size,
+        num_blocks, max_seqlen_q, max_seqlen_k, tile_schedule, num_tiles,
+        nv_paged_prefill_tile_rows(num_q_heads, num_kv_heads), stream);
+    if (st != NV_OK) return st;
+  }
   PrefillArgs a{};
   a.out = out;
   a.q = q;

@@ -301,6 +301,10 @@ extern "C" nv_status nv_sample(int32_t* tokens, const void* logits, int64_t logi
     ps = static_cast<float*>(workspace);
     pi = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align256(n * sizeof(float)));
   }
+  if (nvp_check::on()) {
+    const nv_status st = nvp_check::sample(temperatures, batch, stream);
+    if (st != NV_OK) return st;
+  }
   const int64_t esize = dtype == NV_F32 ? 4 : 2;
   const uintptr_t align = reinterpret_cast<uintptr_t>(logits) |
                           reinterpret_cast<uintptr_t>(gumbel) |

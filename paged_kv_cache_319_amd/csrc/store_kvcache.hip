@@ -81,6 +81,10 @@ extern "C" nv_status nv_store_kvcache(const void* k, const void* v, int64_t k_ro
   const int block = 256;
   const int64_t grid = (threads + block - 1) / block;
   if (grid > 0x7fffffff) return NV_ERR_INVALID_ARG;
+  if (nvp_check::on()) {
+    const nv_status st = nvp_check::store(slot_mapping, num_tokens, num_blocks, block_size, stream);
+    if (st != NV_OK) return st;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const char* kc = static_cast<const char*>(k);
   const char* vc = static_cast<const char*>(v);

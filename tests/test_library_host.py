@@ -47,6 +47,18 @@ def test_exports_every_declared_symbol(lib):
     assert set(SIGNATURES) == names
 
 
+def test_check_mode_toggle_and_message(lib):
+    """Check mode is a process-wide switch (NV_CHECK at the first call, or the setter);
+    the message starts as "no violation".  No GPU call is made."""
+    import os
+    start = lib.nv_set_check_mode(0)
+    assert start == (1 if os.environ.get("NV_CHECK", "0") not in ("", "0") else 0)
+    assert lib.nv_set_check_mode(1) == 0
+    assert lib.nv_set_check_mode(0) == 1
+    assert lib.nv_check_message().decode() == "no violation"
+    lib.nv_set_check_mode(start)
+
+
 def test_status_strings(lib):
     from paged_kv_cache_319_amd import nv_status_string
     assert nv_status_string(0) == "ok"

@@ -465,10 +465,25 @@ def cpu_baseline(case, budget_s=12.0):
             if time.perf_counter() - t0 > budget_s:
                 break
         el = time.perf_counter() - t0
+    alg = sum(decode_bytes(st, sh)[0] for st in case.steps[:steps_done])
     return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"store + decode of the first {steps_done} of {len(case.steps)} steps "
                       f"of the batch-256 workload ({done} decoded tokens), numpy float64, "
-                      f"BLAS limited to 1 thread, {el:.1f} s"}
+                      f"BLAS limited to 1 thread, {el:.1f} s",
+            "gbs": alg / el / 1e9,
+            "cpu_model": cpu_model(),
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():

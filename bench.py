@@ -37,7 +37,7 @@ def parse():
                          "~6 %% slower)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["c3", "c5", "copy", "sampler"], default=None,
+    ap.add_argument("--only", choices=["c3", "c5", "copy", "sampler", "small"], default=None,
                     help="run one leg only (for profiler runs)")
     return ap.parse_args()
 
@@ -258,6 +258,41 @@ def extra_block_size(bs, torch, tp=1):
     del dev
     torch.cuda.empty_cache()
     return out
+
+
+def extra_small_step(torch, reps=200):
+    """The tiny fp32 decode step (4 sequences, lengths 1-200, block size 16): the fused
+    store + decode as eager launches, as replays of its captured HIP graph and as a
+    prepared call (arguments marshalled once), back to back.  At this size launch
+    overhead, not bandwidth, sets the step time."""
+    from workloads import decode_config
+    from paged_kv_cache_319_amd.harness import DeviceDecode
+    case = decode_config("C1")
+    dev = DeviceDecode(case)
+    dev.capture_graphs([0])
+    warm(lambda: dev.step_fused(0), torch)
+    eager = time_region(lambda: dev.step_fused(0), reps, torch)
+    warm(lambda: dev.replay(0), torch)
+    graph = time_region(lambda: dev.replay(0), reps, torch)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dev.step_fused(0)
+    torch.cuda.synchronize()
+    host_eager = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dev.replay(0)
+    torch.cuda.synchronize()
+    host_graph = (time.perf_counter() - t0) / reps
+    launch = dev.prepare_fused(0)
+    warm(launch, torch)
+    prepared = time_region(launch, reps, torch)
+    del dev, launch
+    torch.cuda.empty_cache()
+    return {"c1_fused_eager_us": float(eager * 1e3), "c1_fused_graph_us": float(graph * 1e3),
+            "c1_fused_prepared_us": float(prepared * 1e3),
+            "c1_fused_eager_wall_us": float(host_eager * 1e6),
+            "c1_fused_graph_wall_us": float(host_graph * 1e6)}
 
 
 def extra_block_manager():
@@ -508,6 +543,9 @@ def main():
     if args.only == "sampler":
         print(json.dumps(extra_sampler(torch)), flush=True)
         return
+    if args.only == "small":
+        print(json.dumps(extra_small_step(torch)), flush=True)
+        return
     extra = {}
     print(f"[bench] headline workload: {args.warmup} warmup + {args.steps} timed steps",
           file=sys.stderr, flush=True)
@@ -525,6 +563,8 @@ def main():
         print("[bench] extra head shards", file=sys.stderr, flush=True)
         extra.update(extra_block_size(None, torch, tp=2))
         extra.update(extra_decode("C4", torch, tp=2))
+        print("[bench] extra small step", file=sys.stderr, flush=True)
+        extra.update(extra_small_step(torch))
         print("[bench] extra sampler", file=sys.stderr, flush=True)
         extra.update(extra_sampler(torch))
         extra.update(extra_sampler(torch, dtype="f32"))

@@ -143,13 +143,10 @@ def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     _check("nv_paged_decode", st)
 
 
-def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
-                          v_new: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
-                          v_cache: torch.Tensor, block_tables: torch.Tensor,
-                          context_lens: torch.Tensor, max_context_len: int,
-                          softmax_scale: float, workspace: Optional[torch.Tensor] = None,
-                          stream=None, schedule: Optional[torch.Tensor] = None) -> None:
-    """Store this step's K/V rows and decode, fused into one launch."""
+def _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                       context_lens, max_context_len, softmax_scale, workspace, stream,
+                       schedule):
+    """Validate and marshal the fused store + decode arguments: (C function, args)."""
     nb, bs, hkv, d = k_cache.shape
     batch, hq = q.shape[0], q.shape[1]
     dt = _dtype_code(k_cache)
@@ -167,7 +164,7 @@ def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tenso
         workspace = decode_workspace(k_cache.device, need)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _native.load().nv_paged_decode_store(
+    args = (
         _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new", False), _dev(v_new, "v_new", False),
         k_new.stride(0), v_new.stride(0), _dev(slot_mapping, "slot_mapping"),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -176,7 +173,45 @@ def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tenso
         _dev(schedule, "schedule") if schedule is not None else None,
         max_context_len, batch, hq, hkv, d, nb, bs, float(softmax_scale), dt, ws_ptr, ws_len,
         _stream(stream, q.device))
-    _check("nv_paged_decode_store", st)
+    return _native.load().nv_paged_decode_store, args
+
+
+def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                          v_new: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, block_tables: torch.Tensor,
+                          context_lens: torch.Tensor, max_context_len: int,
+                          softmax_scale: float, workspace: Optional[torch.Tensor] = None,
+                          stream=None, schedule: Optional[torch.Tensor] = None) -> None:
+    """Store this step's K/V rows and decode, fused into one launch."""
+    fn, args = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                  block_tables, context_lens, max_context_len, softmax_scale,
+                                  workspace, stream, schedule)
+    _check("nv_paged_decode_store", fn(*args))
+
+
+def prepare_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                               v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                               k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_tables: torch.Tensor, context_lens: torch.Tensor,
+                               max_context_len: int, softmax_scale: float,
+                               workspace: Optional[torch.Tensor] = None, stream=None,
+                               schedule: Optional[torch.Tensor] = None):
+    """nv_paged_decode_store with its arguments validated and marshalled once: returns a
+    callable that enqueues the same launch again (for steps whose buffers are fixed and
+    refilled in place, where per-call marshalling would dominate a small step).  The
+    callable keeps the tensors alive; the stream is the one current at preparation."""
+    fn, args = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                  block_tables, context_lens, max_context_len, softmax_scale,
+                                  workspace, stream, schedule)
+    cargs = tuple(a if a is None else conv(a) for a, conv in zip(args, fn.argtypes))
+    keep = (out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+            workspace, schedule)
+
+    def launch(_keep=keep):
+        st = fn(*cargs)
+        if st != NV_OK:
+            raise NvError("nv_paged_decode_store", st)
+    return launch
 
 
 # ---------------------------------------------------------------------------

@@ -117,6 +117,16 @@ class DeviceDecode:
                               workspace=self.workspace, schedule=s["schedule"])
         return out
 
+    def prepare_fused(self, t: int):
+        """A callable that enqueues step t's fused store + decode with the arguments
+        marshalled once (nv_paged_decode_store's prepared form)."""
+        from .api import prepare_paged_decode_store
+        s = self.steps[t]
+        return prepare_paged_decode_store(self.out, s["q"], s["k"], s["v"], s["slots"], self.kc,
+                                          self.vc, s["tables"], s["lens"], s["max_len"],
+                                          self.case.shape.scale, workspace=self.workspace,
+                                          schedule=s["schedule"])
+
     def capture_graphs(self, steps=None):
         """Capture one HIP graph per step holding the fused store + decode launch(es).
         All buffers are pre-allocated, so the graphs record kernel nodes only."""

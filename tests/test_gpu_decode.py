@@ -427,3 +427,23 @@ def test_decode_loose_length_bound(dtype, hq, hkv, bs, batch, width):
     want = OracleDecode(case).run_to(0)
     assert_close(got, want, TOL[dtype], f"bound {loose} (longest {tight})")
     assert_close(got, got_tight, TOL[dtype], "loose vs tight bound")
+
+
+def test_prepared_fused_call_matches_eager():
+    """The prepared form of nv_paged_decode_store (arguments marshalled once) enqueues the
+    same launch: outputs and pool bits identical to the eager calls, step after step, and
+    a repeated prepared call of one step gives the same bits again."""
+    from paged_kv_cache_319_amd.harness import DeviceDecode, to_host_bits
+    banner("prepared fused call")
+    case = decode_config("C3", batch=64, steps=3)
+    a = DeviceDecode(case)
+    b = DeviceDecode(case)
+    calls = [b.prepare_fused(t) for t in range(3)]
+    for t in range(3):
+        x = to_host_bits(a.step_fused(t)).copy()
+        calls[t]()
+        assert np.array_equal(x, to_host_bits(b.out))
+    calls[2]()
+    assert np.array_equal(x, to_host_bits(b.out))
+    for p, q in ((a.kc, b.kc), (a.vc, b.vc)):
+        assert np.array_equal(to_host_bits(p).view(np.uint8), to_host_bits(q).view(np.uint8))

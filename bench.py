@@ -37,7 +37,8 @@ def parse():
                          "~6 %% slower)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["c3", "c5", "copy", "sampler", "small"], default=None,
+    ap.add_argument("--only", choices=["c3", "c4", "c5", "copy", "sampler", "small"],
+                    default=None,
                     help="run one leg only (for profiler runs)")
     return ap.parse_args()
 
@@ -542,6 +543,9 @@ def main():
         return
     if args.only == "sampler":
         print(json.dumps(extra_sampler(torch)), flush=True)
+        return
+    if args.only == "c4":
+        print(json.dumps(extra_decode("C4", torch)), flush=True)
         return
     if args.only == "small":
         print(json.dumps(extra_small_step(torch)), flush=True)

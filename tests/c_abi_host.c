@@ -24,7 +24,9 @@
 int main(void) {
   enum { BS = 16, NB = 64, W = 8 };
   CHECK(strcmp(nv_status_string(NV_OK), "ok") == 0);
-  CHECK(nv_set_check_mode(0) >= 0);
+#ifndef NV_HOST_ONLY
+  CHECK(nv_set_check_mode(0) >= 0); /* lives in the GPU part of the library */
+#endif
 
   /* XXH64 of the empty input with seed 0: the algorithm's published value. */
   CHECK(nv_bm_xxh64("", 0, 0) == 0xEF46DB3751D8E999ull);
@@ -66,6 +68,47 @@ int main(void) {
   CHECK(pslots[0] == dtables[20 / BS] * BS + 20 % BS);
 
   CHECK(nv_bm_deallocate(bm, 7) == NV_OK && nv_bm_deallocate(bm, 9) == NV_OK);
+  CHECK(nv_bm_num_free_blocks(bm) == NB);
+  nv_bm_destroy(bm);
+
+  /* Stress: rounds of prompts drawn from a small vocabulary (so prefixes repeat and
+   * blocks are shared), decode steps that open new blocks, and releases, until the
+   * pool is exhausted and refilled many times; every block must come back. */
+  CHECK(nv_bm_create(NB, BS, &bm) == NV_OK);
+  uint32_t rng = 12345u;
+  int32_t prompt[6 * BS];
+  int64_t live[8];
+  int nlive = 0;
+  for (int round = 0; round < 400; ++round) {
+    rng = rng * 1664525u + 1013904223u;
+    if (nlive < 8 && (rng >> 28) < 10) {
+      const int32_t len = 1 + (int32_t)((rng >> 8) % (6 * BS - 1));
+      for (int i = 0; i < len; ++i)
+        prompt[i] = (int32_t)((i < 2 * BS) ? (uint32_t)(i % 7) : (rng >> (i % 16)) % 5u);
+      int32_t ok = 0;
+      CHECK(nv_bm_can_allocate(bm, len, &ok) == NV_OK);
+      if (ok) {
+        int32_t nc = -1;
+        CHECK(nv_bm_allocate(bm, 1000 + round, prompt, len, &nc) == NV_OK);
+        CHECK(nc >= 0 && nc < len && nc % BS == 0);
+        live[nlive++] = 1000 + round;
+      } else {
+        CHECK(nv_bm_allocate(bm, 1000 + round, prompt, len, NULL) != NV_OK ||
+              nv_bm_deallocate(bm, 1000 + round) == NV_OK);
+      }
+    } else if (nlive > 0 && (rng >> 29) < 6) {
+      for (int j = 0; j < nlive; ++j) {
+        int32_t ok = 0;
+        CHECK(nv_bm_can_append(bm, live[j], &ok) == NV_OK);
+        if (ok) CHECK(nv_bm_append_token(bm, live[j], (int32_t)(rng % 5)) == NV_OK);
+      }
+    } else if (nlive > 0) {
+      const int j = (int)((rng >> 4) % (uint32_t)nlive);
+      CHECK(nv_bm_deallocate(bm, live[j]) == NV_OK);
+      live[j] = live[--nlive];
+    }
+  }
+  while (nlive > 0) CHECK(nv_bm_deallocate(bm, live[--nlive]) == NV_OK);
   CHECK(nv_bm_num_free_blocks(bm) == NB);
   nv_bm_destroy(bm);
   printf("c abi ok\n");

@@ -51,7 +51,8 @@ def test_sampler_full_workload(dtype):
 
 
 @pytest.mark.parametrize("batch,vocab", [(1, 1), (1, 13), (3, 1000), (5, 4099), (2, 70001),
-                                         (1, 151936), (7, 32000), (300, 4096), (64, 8191)])
+                                         (1, 151936), (7, 32000), (300, 4096), (64, 8191),
+                                         (65535, 257)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_sampler_ragged_shapes(batch, vocab, dtype):
     banner(f"sampler ragged batch {batch} vocab {vocab} {dtype}")

@@ -71,10 +71,7 @@ def _ptr(a: np.ndarray):
 # store_kvcache
 # ---------------------------------------------------------------------------
 
-def nv_store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
-                     v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
-    """k, v: [N, Hkv, D] (rows may be strided, heads and dims contiguous);
-    caches: [num_blocks, block_size, Hkv, D]; slot_mapping: int32 [N] on the device."""
+def _store_call(k, v, k_cache, v_cache, slot_mapping, stream):
     nb, bs, hkv, d = k_cache.shape
     n = k.shape[0]
     for name, t in (("k", k), ("v", v)):
@@ -82,11 +79,38 @@ def nv_store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
             raise ValueError(f"{name} must be [N, {hkv}, {d}] with contiguous heads")
     if slot_mapping.dtype != torch.int32 or slot_mapping.numel() != n:
         raise ValueError("slot_mapping must be int32 with one entry per row")
-    st = _native.load().nv_store_kvcache(
-        _dev(k, "k", False), _dev(v, "v", False), k.stride(0), v.stride(0),
-        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"),
-        n, hkv, d, nb, bs, _dtype_code(k_cache), _stream(stream, k_cache.device))
-    _check("nv_store_kvcache", st)
+    args = (_dev(k, "k", False), _dev(v, "v", False), k.stride(0), v.stride(0),
+            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping"),
+            n, hkv, d, nb, bs, _dtype_code(k_cache), _stream(stream, k_cache.device))
+    return _native.load().nv_store_kvcache, args
+
+
+def nv_store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                     v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """k, v: [N, Hkv, D] (rows may be strided, heads and dims contiguous);
+    caches: [num_blocks, block_size, Hkv, D]; slot_mapping: int32 [N] on the device."""
+    fn, args = _store_call(k, v, k_cache, v_cache, slot_mapping, stream)
+    _check("nv_store_kvcache", fn(*args))
+
+
+def _prepared(name, fn, args, keep):
+    """A callable that repeats one C call with arguments converted to ctypes once."""
+    cargs = tuple(a if a is None else conv(a) for a, conv in zip(args, fn.argtypes))
+
+    def launch(_keep=keep):
+        st = fn(*cargs)
+        if st != NV_OK:
+            raise NvError(name, st)
+    return launch
+
+
+def prepare_store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None):
+    """nv_store_kvcache with its arguments validated and marshalled once: returns a
+    callable that enqueues the same store again (buffers refilled in place).  The
+    callable keeps the tensors alive; the stream is the one current at preparation."""
+    fn, args = _store_call(k, v, k_cache, v_cache, slot_mapping, stream)
+    return _prepared("nv_store_kvcache", fn, args, (k, v, k_cache, v_cache, slot_mapping))
 
 
 # ---------------------------------------------------------------------------
@@ -203,15 +227,9 @@ def prepare_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.
     fn, args = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
                                   block_tables, context_lens, max_context_len, softmax_scale,
                                   workspace, stream, schedule)
-    cargs = tuple(a if a is None else conv(a) for a, conv in zip(args, fn.argtypes))
     keep = (out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
             workspace, schedule)
-
-    def launch(_keep=keep):
-        st = fn(*cargs)
-        if st != NV_OK:
-            raise NvError("nv_paged_decode_store", st)
-    return launch
+    return _prepared("nv_paged_decode_store", fn, args, keep)
 
 
 # ---------------------------------------------------------------------------

@@ -117,6 +117,12 @@ class DeviceDecode:
                               workspace=self.workspace, schedule=s["schedule"])
         return out
 
+    def prepare_store(self, t: int):
+        """A callable that enqueues step t's store with the arguments marshalled once."""
+        from .api import prepare_store_kvcache
+        s = self.steps[t]
+        return prepare_store_kvcache(s["k"], s["v"], self.kc, self.vc, s["slots"])
+
     def prepare_fused(self, t: int):
         """A callable that enqueues step t's fused store + decode with the arguments
         marshalled once (nv_paged_decode_store's prepared form)."""
@@ -169,6 +175,11 @@ class DevicePrefill:
 
     def store(self):
         nv_store_kvcache(self.k, self.v, self.kc, self.vc, self.slots)
+
+    def prepare_store(self):
+        """A callable that enqueues this workload's store with the arguments marshalled once."""
+        from .api import prepare_store_kvcache
+        return prepare_store_kvcache(self.k, self.v, self.kc, self.vc, self.slots)
 
     def attend(self, out=None):
         out = self.out if out is None else out

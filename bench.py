@@ -225,7 +225,8 @@ def extra_decode(name, torch, reps=50, tp=1):
     ms = time_region(lambda: dev.decode(0), reps, torch)
     tag = name.lower() if tp == 1 else f"{name.lower()}_tp{tp}_shard"
     out = {f"{tag}_decode_us": float(ms * 1e3),
-           f"{tag}_decode_gbs": float(b / (ms * 1e-3) / 1e9)}
+           f"{tag}_decode_gbs": float(b / (ms * 1e-3) / 1e9),
+           f"{tag}_decode_hbm_frac": float(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS)}
     del dev
     torch.cuda.empty_cache()
     return out
@@ -363,7 +364,8 @@ def extra_prefill(torch, reps=20, bs=None):
            f"{tag}_prefill_tflops": float(flops / (at * 1e-3) / 1e12),
            f"{tag}_prefill_mfma_frac": float(flops / (at * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
            f"{tag}_store_us": float(st * 1e3),
-           f"{tag}_store_gbs": float(sbytes / (st * 1e-3) / 1e9)}
+           f"{tag}_store_gbs": float(sbytes / (st * 1e-3) / 1e9),
+           f"{tag}_store_hbm_frac": float(sbytes / (st * 1e-3) / 1e9 / HBM_PEAK_GBS)}
     del dev
     torch.cuda.empty_cache()
     return out

@@ -8,11 +8,12 @@
 //
 // The work is one streaming pass over [batch, vocab] logits (and the noise of
 // rows with T > 0), so it is bound by HBM bandwidth.  Each row is cut into
-// `chunks` contiguous pieces; workgroup (chunk, row) streams its piece with
-// 16-byte non-temporal loads, eight elements per lane and step, keeps the best
-// (score, index) per lane and reduces it over the workgroup.  With one chunk per
-// row the workgroup writes the token; otherwise it writes a partial pair and a
-// second kernel reduces the chunks of each row.
+// `chunks` contiguous pieces (one piece per row when the batch alone fills the
+// chip); workgroup (chunk, row) streams its piece with 16-byte non-temporal loads,
+// eight elements per lane and step, keeps the best (score, index) per lane and
+// reduces it over the workgroup.  With one chunk per row the workgroup writes the
+// token; otherwise it writes a partial pair and a second kernel reduces the chunks
+// of each row.
 //
 // Scores are binary32: s = (z / T) + g, with a correctly rounded division and
 // addition, so the argmax is a well-defined function of the inputs.  Ties go to
@@ -24,9 +25,14 @@
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnit = 8;     // elements per lane-step
-constexpr int kUnroll = 4;   // lane-steps whose loads are issued together
+constexpr int kThreads = 256;  // split plans and the merge kernel
+constexpr int kUnit = 8;       // elements per lane-step
+constexpr int kUnroll = 4;     // split plans: lane-steps whose loads are issued together
+// Batches of at least kRowPlanBatch rows: one kRowThreads-thread workgroup per row
+// (enough rows to fill the chip), kRowUnroll lane-steps in flight, no merge.
+constexpr int kRowPlanBatch = 256;
+constexpr int kRowThreads = 1024;
+constexpr int kRowUnroll = 2;
 
 struct Best {
   float s;
@@ -56,10 +62,11 @@ __device__ __forceinline__ Best wave_best(Best b) {
   return b;
 }
 
-// Best over the workgroup; the result is valid in thread 0.
+// Best over the workgroup of NT threads; the result is valid in thread 0.
+template <int NT>
 __device__ __forceinline__ Best block_best(Best b) {
-  __shared__ float ss[kThreads / nvp::kWave];
-  __shared__ int32_t si[kThreads / nvp::kWave];
+  __shared__ float ss[NT / nvp::kWave];
+  __shared__ int32_t si[NT / nvp::kWave];
   b = wave_best(b);
   const int w = threadIdx.x / nvp::kWave;
   if ((threadIdx.x & (nvp::kWave - 1)) == 0) {
@@ -69,7 +76,7 @@ __device__ __forceinline__ Best block_best(Best b) {
   __syncthreads();
   if (threadIdx.x == 0) {
 #pragma unroll
-    for (int k = 1; k < kThreads / nvp::kWave; ++k) take(b, ss[k], si[k]);
+    for (int k = 1; k < NT / nvp::kWave; ++k) take(b, ss[k], si[k]);
   }
   return b;
 }
@@ -126,7 +133,7 @@ __device__ __forceinline__ float score(float z, float t, float g) {
 // first of equal scores; a lane whose scores are all -inf reports its first index.
 // VEC: row bases and strides are 16-byte aligned, so lane-steps of eight elements
 // are read with 16-byte loads; otherwise every element is loaded on its own.
-template <typename DT, bool VEC, bool GREEDY>
+template <typename DT, bool VEC, bool GREEDY, int NT, int UNROLL>
 __device__ __forceinline__ Best scan(const typename DT::T* __restrict__ zr,
                                      const float* __restrict__ gr, float t, int32_t lo,
                                      int32_t hi) {
@@ -139,18 +146,18 @@ __device__ __forceinline__ Best scan(const typename DT::T* __restrict__ zr,
     tail = lo + steps * kUnit;
     int32_t u = threadIdx.x;
     if (u < steps) first = lo + u * kUnit;
-    for (; u + (kUnroll - 1) * kThreads < steps; u += kUnroll * kThreads) {
-      Logits8<DT> z[kUnroll];
-      Noise8 g[kUnroll];
+    for (; u + (UNROLL - 1) * NT < steps; u += UNROLL * NT) {
+      Logits8<DT> z[UNROLL];
+      Noise8 g[UNROLL];
 #pragma unroll
-      for (int k = 0; k < kUnroll; ++k) z[k].load(zr + lo + (u + k * kThreads) * kUnit);
+      for (int k = 0; k < UNROLL; ++k) z[k].load(zr + lo + (u + k * NT) * kUnit);
       if constexpr (!GREEDY) {
 #pragma unroll
-        for (int k = 0; k < kUnroll; ++k) g[k].load(gr + lo + (u + k * kThreads) * kUnit);
+        for (int k = 0; k < UNROLL; ++k) g[k].load(gr + lo + (u + k * NT) * kUnit);
       }
 #pragma unroll
-      for (int k = 0; k < kUnroll; ++k) {
-        const int32_t base = lo + (u + k * kThreads) * kUnit;
+      for (int k = 0; k < UNROLL; ++k) {
+        const int32_t base = lo + (u + k * NT) * kUnit;
 #pragma unroll
         for (int e = 0; e < kUnit; ++e) {
           const float s = score<GREEDY>(z[k].at(e), t, GREEDY ? 0.0f : g[k].at(e));
@@ -160,7 +167,7 @@ __device__ __forceinline__ Best scan(const typename DT::T* __restrict__ zr,
         }
       }
     }
-    for (; u < steps; u += kThreads) {
+    for (; u < steps; u += NT) {
       Logits8<DT> z;
       Noise8 g;
       z.load(zr + lo + u * kUnit);
@@ -177,7 +184,7 @@ __device__ __forceinline__ Best scan(const typename DT::T* __restrict__ zr,
   }
   if (first == INT32_MAX && tail + static_cast<int32_t>(threadIdx.x) < hi)
     first = tail + threadIdx.x;
-  for (int32_t i = tail + threadIdx.x; i < hi; i += kThreads) {
+  for (int32_t i = tail + threadIdx.x; i < hi; i += NT) {
     float z;
     if constexpr (sizeof(typename DT::T) == 2)
       z = nvp::bf16_lo(static_cast<uint32_t>(zr[i]));
@@ -192,8 +199,8 @@ __device__ __forceinline__ Best scan(const typename DT::T* __restrict__ zr,
   return Best{bs, bi};
 }
 
-template <typename DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_partial_kernel(
+template <typename DT, bool VEC, int NT, int UNROLL>
+__global__ __launch_bounds__(NT) void sample_partial_kernel(
     const typename DT::T* __restrict__ logits, int64_t logits_stride,
     const float* __restrict__ temperatures, const float* __restrict__ gumbel,
     int64_t gumbel_stride, int32_t vocab, int32_t chunk, int32_t chunks,
@@ -207,9 +214,9 @@ __global__ __launch_bounds__(kThreads) void sample_partial_kernel(
   const float t = temperatures[row];
   const typename DT::T* zr = logits + static_cast<int64_t>(row) * logits_stride;
   const float* gr = gumbel + static_cast<int64_t>(row) * gumbel_stride;
-  Best best = t == 0.0f ? scan<DT, VEC, true>(zr, gr, t, lo, hi)
-                        : scan<DT, VEC, false>(zr, gr, t, lo, hi);
-  best = block_best(best);
+  Best best = t == 0.0f ? scan<DT, VEC, true, NT, UNROLL>(zr, gr, t, lo, hi)
+                        : scan<DT, VEC, false, NT, UNROLL>(zr, gr, t, lo, hi);
+  best = block_best<NT>(best);
   if (threadIdx.x == 0) {
     if (chunks == 1) {
       tokens[row] = best.i;
@@ -235,10 +242,12 @@ __global__ __launch_bounds__(kThreads) void sample_merge_kernel(
   if (lane == 0) tokens[row] = best.i;
 }
 
-// Work split: enough workgroups to cover the chip many times over, each
-// streaming at least kMinChunk elements; chunk lengths are multiples of kUnit.
-// Batch 256 x 151,936 with a flushed cache: 2048 groups 45.3 us, 4096 42.8 us,
-// 8192 (32 chunks of 4752 per row) 41.8 us.
+// Work split.  Batches of kRowPlanBatch rows or more: one wide workgroup per row
+// (batch 256 x 151,936, flushed cache: 40.8 us against 41.8 for the best split; an
+// all-greedy batch 13.8 against 20.6 us).  Smaller batches: enough workgroups to
+// cover the chip many times over, each streaming at least kMinChunk elements, chunk
+// lengths multiples of kUnit (batch 256 split into 2048 groups 45.3 us, 4096 42.8,
+// 8192 41.8), and a merge kernel.
 constexpr int64_t kTargetGroups = 8192;
 constexpr int32_t kMinChunk = 4096;
 
@@ -248,6 +257,10 @@ struct Plan {
 };
 
 Plan plan_for(int32_t batch, int32_t vocab) {
+  if (batch >= kRowPlanBatch) {
+    const int64_t chunk = (static_cast<int64_t>(vocab) + kUnit - 1) / kUnit * kUnit;
+    return Plan{static_cast<int32_t>(chunk), 1};
+  }
   int64_t want = (kTargetGroups + batch - 1) / batch;
   const int64_t most = (static_cast<int64_t>(vocab) + kMinChunk - 1) / kMinChunk;
   if (want > most) want = most;
@@ -264,9 +277,15 @@ template <typename DT, bool VEC>
 void launch_partial(const void* logits, int64_t ls, const float* temps, const float* gumbel,
                     int64_t gs, int32_t vocab, const Plan& p, int32_t batch, float* ps,
                     int32_t* pi, int32_t* tokens, hipStream_t s) {
-  sample_partial_kernel<DT, VEC><<<dim3(p.chunks, batch), dim3(kThreads), 0, s>>>(
-      static_cast<const typename DT::T*>(logits), ls, temps, gumbel, gs, vocab, p.chunk,
-      p.chunks, ps, pi, tokens);
+  const auto* z = static_cast<const typename DT::T*>(logits);
+  if (batch >= kRowPlanBatch)
+    sample_partial_kernel<DT, VEC, kRowThreads, kRowUnroll>
+        <<<dim3(p.chunks, batch), dim3(kRowThreads), 0, s>>>(z, ls, temps, gumbel, gs, vocab,
+                                                             p.chunk, p.chunks, ps, pi, tokens);
+  else
+    sample_partial_kernel<DT, VEC, kThreads, kUnroll>
+        <<<dim3(p.chunks, batch), dim3(kThreads), 0, s>>>(z, ls, temps, gumbel, gs, vocab,
+                                                          p.chunk, p.chunks, ps, pi, tokens);
 }
 
 }  // namespace
@@ -287,7 +306,7 @@ extern "C" nv_status nv_sample(int32_t* tokens, const void* logits, int64_t logi
   if (batch < 0 || vocab <= 0) return NV_ERR_INVALID_ARG;
   if (dtype != NV_F32 && dtype != NV_BF16) return NV_ERR_UNSUPPORTED;
   if (batch == 0) return NV_OK;
-  if (batch > 65535) return NV_ERR_UNSUPPORTED;  // one grid row per batch row
+  if (batch > 65535 || vocab > 0x7fffff00) return NV_ERR_UNSUPPORTED;  // grid rows; int32 chunks
   if (!tokens || !logits || !temperatures || !gumbel) return NV_ERR_INVALID_ARG;
   if (logits_row_stride < vocab || gumbel_row_stride < vocab) return NV_ERR_INVALID_ARG;
   const Plan p = plan_for(batch, vocab);

@@ -163,10 +163,11 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.nv_paged_prefill_tile_rows(12, 8) == 0
     # sampler: short stride, bad dtype, null noise, too-small workspace, batch 0
     V = 151936
-    n = lib.nv_sample_workspace_size(256, V)
-    assert n >= 256 * 8 * 8                                         # split rows: partials
-    assert lib.nv_sample_workspace_size(300, 4096) == 0             # one workgroup per row
-    smp = lambda **kw: [p, p, kw.get("ls", V), p, kw.get("g", p), V, kw.get("B", 256), V,
+    n = lib.nv_sample_workspace_size(64, V)
+    assert n >= 64 * 32 * 8                                         # split rows: partials
+    assert lib.nv_sample_workspace_size(256, V) == 0                # one workgroup per row
+    assert lib.nv_sample_workspace_size(8, 4096) == 0               # one chunk per row
+    smp = lambda **kw: [p, p, kw.get("ls", V), p, kw.get("g", p), V, kw.get("B", 64), V,
                         kw.get("dt", 1), kw.get("ws", p), kw.get("wsn", n), s]
     assert lib.nv_sample(*smp(ls=V - 1)) == -1
     assert lib.nv_sample(*smp(dt=2)) == -2

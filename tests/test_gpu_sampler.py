@@ -139,3 +139,26 @@ def test_sampler_workspace_reuse_across_shapes():
         torch.cuda.synchronize()
         want = oracle.sample(case.logits, case.temperatures, case.gumbel)
         assert np.array_equal(tok.cpu().numpy().astype(np.int64), want), (b, v)
+
+
+@pytest.mark.parametrize("t", [0.5, 1.0, 2.0])
+def test_sampler_token_frequencies_follow_softmax(t):
+    """The GPU path against the Gumbel-max theorem directly: 65 535 copies of one logit row
+    with independent noise; token frequencies within 5 standard errors of softmax(z / T)."""
+    from paged_kv_cache_319_amd import nv_sample, nv_sample_workspace_size
+    banner(f"sampler frequencies T={t}")
+    z = np.array([1.0, 0.5, 0.0, -0.5, 2.0, 1.5, -1.0, 0.25], dtype=np.float32)
+    B = 65535
+    rng = np.random.default_rng(31)
+    logits = torch.from_numpy(np.tile(z, (B, 1))).cuda()
+    gumbel = torch.from_numpy(rng.gumbel(size=(B, z.size)).astype(np.float32)).cuda()
+    temps = torch.full((B,), t, dtype=torch.float32, device="cuda")
+    tok = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(max(nv_sample_workspace_size(B, z.size), 1), dtype=torch.uint8,
+                     device="cuda")
+    nv_sample(tok, logits, temps, gumbel, workspace=ws)
+    freq = np.bincount(tok.cpu().numpy(), minlength=z.size) / B
+    e = np.exp((z.astype(np.float64) - z.max()) / t)
+    p = e / e.sum()
+    se = np.sqrt(p * (1 - p) / B)
+    assert np.all(np.abs(freq - p) <= 5 * se), (freq, p)

@@ -7,11 +7,18 @@ U[100, 1024] at step 0, 16 query / 8 KV heads, head_dim 128, block size 256, bf1
 50 successive decode steps that each append one token per sequence (a new block is
 taken when a token opens one).  One benchmark step = one decode step of that
 sequence: the store of the 256 new K/V rows and the decode, fused in one
-nv_paged_decode_store launch.  Steps cycle through the 50 steps.  All inputs (pool, tables, slots, schedule, q, new rows) are
+nv_paged_decode_store launch.  Steps cycle through the 50 steps; the timed region
+starts at step 0.  All inputs (pool, tables, slots, schedule, q, new rows) are
 resident in HBM before timing starts; the host builds no metadata in the timed loop.
 
+Warm-up: at least --warmup steps AND at least WARMUP_FLOOR_S seconds of back-to-back
+steps, in whole passes over the 50 steps (the chip runs its first ~10 ms of work after
+the host-side set-up several per cent slower).  The line records the steps and the time
+the warm-up actually took, and the first pass's per-launch time is kept in "extra".
+
 Prints ONE JSON line.  Extra measurements (other workloads, cold-cache kernel time)
-go into the same line under "extra".
+go into the same line under "extra"; a failing extra leg records "<leg>_error" there
+instead of ending the run.
 """
 from __future__ import annotations
 
@@ -20,27 +27,36 @@ import json
 import os
 import sys
 import time
+import traceback
 
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+WARMUP_FLOOR_S = 0.1           # least wall time of warm-up steps before the timed region
+MAX_CPU_WORKERS = 16           # the GPU machine's host-CPU share per GPU
+DECODE_KERNEL = "paged_decode_kernel<BF16,128,2,4,fast,store,2>"
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=500,
-                    help="untimed steps first (default: ten passes over the 50-step workload, "
-                         "~45 ms of GPU work: the first ~10 ms after the host-side set-up run "
-                         "~6 %% slower)")
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="least number of untimed steps first (the warm-up also lasts at "
+                         f"least {WARMUP_FLOOR_S * 1e3:.0f} ms, in whole passes of the "
+                         "50-step workload)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=["c3", "c4", "c5", "copy", "sampler", "small"],
                     default=None,
-                    help="run one leg only (for profiler runs)")
-    return ap.parse_args()
+                    help="run one leg only (for profiler runs); c3 = the headline alone")
+    args = ap.parse_args(argv)
+    if args.steps < 1:
+        ap.error("--steps must be >= 1")
+    if args.warmup < 0:
+        ap.error("--warmup must be >= 0")
+    return args
 
 
 # ---------------------------------------------------------------------------
@@ -73,118 +89,34 @@ def decode_flops(step, shape):
     return 4.0 * shape.num_q_heads * shape.head_dim * float(np.sum(step.context_lens))
 
 
+def store_bytes(shape, rows):
+    """K and V rows read and written, plus the slots."""
+    return 2 * 2 * rows * shape.num_kv_heads * shape.head_dim * shape.elem_bytes + 4 * rows
+
+
 # ---------------------------------------------------------------------------
-# GPU legs
+# step order, warm-up and timing helpers (no GPU specifics: the tests drive them with
+# a stand-in device)
 # ---------------------------------------------------------------------------
 
-def time_fused_steps(dev, steps_idx, torch, flush=None, graphs=True):
-    """Fused store + decode (nv_paged_decode_store), one launch per step, replayed from the
-    step's captured HIP graph (or called eagerly); per-step ms from HIP events recorded on
-    the stream the graph is launched on."""
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in steps_idx]
-    for (a, b), t in zip(ev, steps_idx):
-        if flush is not None:
-            flush()
-        a.record(stream)
-        if graphs:
-            dev.replay(t)
-        else:
-            dev.step_fused(t)
-        b.record(stream)
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in ev]
+def cycle(nsteps, n, start=0):
+    """n step indices cycling over the workload's nsteps steps from ``start``."""
+    return [(start + i) % nsteps for i in range(n)]
 
 
-def headline(args, torch, extra):
-    from workloads import decode_config
-    from paged_kv_cache_319_amd.harness import DeviceDecode
-    case = decode_config("C3")
-    sh = case.shape
-    nsteps = len(case.steps)
-    dev = DeviceDecode(case, poison=True)
-    acct = [decode_bytes(st, sh) for st in case.steps]
-    flops = [decode_flops(st, sh) for st in case.steps]
-    B = case.batch
-    row = sh.num_kv_heads * sh.head_dim * sh.elem_bytes
-    store_bytes = 2 * 2 * B * row + 4 * B          # K and V rows read + written, slots
-
-    # warmup
-    for i in range(args.warmup):
-        dev.step_fused(i % nsteps)
-    torch.cuda.synchronize()
-
-    # Timed region: exactly K steps, each the fused store + decode of one step, back to
-    # back on the stream.  One HIP event pair on that stream brackets the K launches (an
-    # event pair per launch would add several microseconds of stream time to each), so
-    # event time / K is the kernel's average launch duration; the host clock around the
-    # same region (synchronised on both sides) gives the value.
-    order = [(args.warmup + i) % nsteps for i in range(args.steps)]
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for t in order:
-        dev.step_fused(t)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    launch_ms = ev0.elapsed_time(ev1) / args.steps
-    alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64) + store_bytes
-    log_bytes = np.array([acct[t][1] for t in order], dtype=np.float64)
-    fl = np.array([flops[t] for t in order])
-    span_s = launch_ms * 1e-3 * args.steps
-    gbs = alg_bytes.sum() / span_s / 1e9
-    # Spread of single launches: the same steps with an event pair around each launch
-    # (these durations include the event overhead).
-    step_ms = np.array(time_fused_steps(dev, order, torch, graphs=False))
-    res = dict(
-        value=B * args.steps / wall, wall=wall,
-        ms_per_step=wall * 1e3 / args.steps,
-        kernel_us_mean=launch_ms * 1e3,
-        per_launch_event_us_p10=float(np.percentile(step_ms, 10) * 1e3),
-        per_launch_event_us_p50=float(np.percentile(step_ms, 50) * 1e3),
-        per_launch_event_us_p90=float(np.percentile(step_ms, 90) * 1e3),
-        alg_bytes_per_launch=float(alg_bytes.mean()),
-        gbs=gbs,
-        effective_kv_gbs=float(log_bytes.sum() / span_s / 1e9),
-        tflops=float(fl.sum() / span_s / 1e12),
-        kernel_tokens_per_s=float(B / (launch_ms * 1e-3)),
-    )
-
-    if not args.no_extra:
-        # The same fused steps replayed from per-step HIP graphs.
-        dev.capture_graphs()
-        it = iter(order[:50])
-        extra["c3_fused_graph_replay_us"] = float(
-            time_region(lambda: dev.replay(next(it)), 50, torch) * 1e3)
-        # The same steps as two launches (nv_store_kvcache, then nv_paged_decode), each
-        # kind timed over back-to-back launches of the 50 steps.
-        stores = {t: dev.prepare_store(t) for t in set(order[:50])}
-        it = iter(order[:50] * 2)
-        st_ms = time_region(lambda: stores[next(it)](), 50, torch)
-        it = iter(order[:50])
-        de_ms = time_region(lambda: dev.decode(next(it)), 50, torch)
-        db = np.array([acct[t][0] for t in order[:50]])
-        extra["c3_separate_store_us"] = float(st_ms * 1e3)
-        extra["c3_separate_decode_us"] = float(de_ms * 1e3)
-        extra["c3_separate_decode_gbs"] = float(db.mean() / (de_ms * 1e-3) / 1e9)
-        extra["c3_separate_store_gbs"] = float(store_bytes / (st_ms * 1e-3) / 1e9)
-        # Cold-cache kernel times: reading a 1 GiB buffer between steps (outside the
-        # events) leaves L2 and the 256 MB MALL holding only clean lines of that buffer.
-        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-        cold = np.array(time_fused_steps(dev, order[:20], torch, graphs=False,
-                                         flush=lambda: scratch.sum()))
-        cb = np.array([acct[t][0] for t in order[:20]]) + store_bytes
-        extra["c3_fused_cold_us_mean"] = float(cold.mean() * 1e3)
-        extra["c3_fused_cold_gbs"] = float(cb.sum() / (cold.sum() * 1e-3) / 1e9)
-        del scratch
-    del dev
-    torch.cuda.empty_cache()
-    return case, res
+def warm_up(launch, nsteps, min_steps, floor_s, sync, clock=time.perf_counter):
+    """Launch whole passes over steps 0 .. nsteps-1 until at least ``min_steps`` steps
+    and ``floor_s`` seconds have gone by; returns (steps launched, seconds).  Ending on a
+    pass boundary means the next step is step 0 and every earlier row is stored."""
+    t0 = clock()
+    done = 0
+    while True:
+        for t in range(nsteps):
+            launch(t)
+        done += nsteps
+        sync()
+        if done >= min_steps and clock() - t0 >= floor_s:
+            return done, clock() - t0
 
 
 def time_region(fn, reps, torch):
@@ -201,16 +133,148 @@ def time_region(fn, reps, torch):
     return a.elapsed_time(b) / reps
 
 
+def time_each(launches, torch, flush=None):
+    """Per-launch ms from an event pair around each launch (each pair adds its own
+    overhead), optionally with ``flush()`` before each pair, outside the events."""
+    stream = torch.cuda.current_stream()
+    ev = []
+    for fn in launches:
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def warm(fn, torch, seconds=0.05):
-    """Run fn back to back for `seconds` of wall time: after the host-side set-up of a
-    workload the GPU runs its first ~10 ms of work up to 10 % slower."""
-    import time
+    """Run fn back to back for `seconds` of wall time before an extra leg is timed."""
     t_end = time.perf_counter() + seconds
     while time.perf_counter() < t_end:
         for _ in range(10):
             fn()
         torch.cuda.synchronize()
 
+
+def guarded(extra, name, fn, *a, **kw):
+    """Run one extra leg; merge its dict into ``extra`` or record ``<name>_error``."""
+    try:
+        res = fn(*a, **kw)
+        if res:
+            extra.update(res)
+    except Exception as e:  # an extra leg never discards the headline
+        extra[f"{name}_error"] = f"{type(e).__name__}: {e}"
+        traceback.print_exc(file=sys.stderr)
+
+
+# ---------------------------------------------------------------------------
+# the headline: fused store + decode of the batch-256 workload
+# ---------------------------------------------------------------------------
+
+def headline(args, torch, extra, case, dev):
+    """Warm-up, then exactly args.steps back-to-back fused steps from step 0."""
+    sh = case.shape
+    nsteps = len(case.steps)
+    B = case.batch
+    acct = [decode_bytes(st, sh) for st in case.steps]
+    flops = [decode_flops(st, sh) for st in case.steps]
+    sbytes = store_bytes(sh, B)
+    # One prepared call per step: arguments validated and marshalled once, so the host
+    # spends a few microseconds per launch (the kernel takes ~80).
+    launches = [dev.prepare_fused(t) for t in range(nsteps)]
+
+    # The first pass after set-up, event-timed, then the rest of the warm-up.
+    first_ms = time_region_seq([launches[t] for t in range(nsteps)], torch)
+    w_steps, w_s = warm_up(lambda t: launches[t](), nsteps, max(0, args.warmup - nsteps),
+                           WARMUP_FLOOR_S, torch.cuda.synchronize)
+    warm_steps = nsteps + w_steps
+    warm_ms = first_ms * nsteps + w_s * 1e3
+
+    # Timed region: exactly K steps, back to back on the stream.  One HIP event pair on
+    # that stream brackets the K launches, so event time / K is the kernel's average
+    # launch duration; the host clock around the same region (synchronised on both
+    # sides) gives the value.
+    order = cycle(nsteps, args.steps)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for t in order:
+        launches[t]()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = ev0.elapsed_time(ev1) / args.steps
+    alg_bytes = np.array([acct[t][0] for t in order], dtype=np.float64) + sbytes
+    log_bytes = np.array([acct[t][1] for t in order], dtype=np.float64)
+    fl = np.array([flops[t] for t in order])
+    span_s = launch_ms * 1e-3 * args.steps
+    gbs = alg_bytes.sum() / span_s / 1e9
+    # Spread of single launches: the same steps with an event pair around each launch.
+    step_ms = np.array(time_each([launches[t] for t in order], torch))
+    extra.update({
+        "c3_first_pass_us_mean": float(first_ms * 1e3),
+        "c3_first_pass_gbs": float((np.mean([a[0] for a in acct]) + sbytes) / (first_ms * 1e-3) / 1e9),
+        "kernel_us_mean": float(launch_ms * 1e3),
+        "per_launch_event_us_p10": float(np.percentile(step_ms, 10) * 1e3),
+        "per_launch_event_us_p50": float(np.percentile(step_ms, 50) * 1e3),
+        "per_launch_event_us_p90": float(np.percentile(step_ms, 90) * 1e3),
+        "alg_bytes_per_launch": float(alg_bytes.mean()),
+        "effective_kv_gbs": float(log_bytes.sum() / span_s / 1e9),
+        "tflops": float(fl.sum() / span_s / 1e12),
+        "kernel_tokens_per_s": float(B / (launch_ms * 1e-3)),
+    })
+    return dict(value=B * args.steps / wall, wall=wall, ms_per_step=wall * 1e3 / args.steps,
+                gbs=gbs, warmup_steps=warm_steps, warmup_ms=warm_ms)
+
+
+def time_region_seq(launches, torch):
+    """Mean ms of one launch over a list of different launches, back to back, one event
+    pair around all of them."""
+    it = iter(launches)
+    return time_region(lambda: next(it)(), len(launches), torch)
+
+
+def extra_c3(torch, case, dev, reps=50):
+    """The headline steps in other forms, each over `reps` steps cycling from step 0:
+    replays of per-step HIP graphs, the store and the decode as separate launches, and
+    fused launches with a cold cache."""
+    sh = case.shape
+    nsteps = len(case.steps)
+    order = cycle(nsteps, reps)
+    out = {}
+    dev.capture_graphs()
+    out["c3_fused_graph_replay_us"] = float(
+        time_region_seq([lambda t=t: dev.replay(t) for t in order], torch) * 1e3)
+    stores = {t: dev.prepare_store(t) for t in set(order)}
+    st_ms = time_region_seq([stores[t] for t in order], torch)
+    de_ms = time_region_seq([lambda t=t: dev.decode(t) for t in order], torch)
+    db = np.array([decode_bytes(case.steps[t], sh)[0] for t in order])
+    sb = store_bytes(sh, case.batch)
+    out["c3_separate_store_us"] = float(st_ms * 1e3)
+    out["c3_separate_decode_us"] = float(de_ms * 1e3)
+    out["c3_separate_decode_gbs"] = float(db.mean() / (de_ms * 1e-3) / 1e9)
+    out["c3_separate_store_gbs"] = float(sb / (st_ms * 1e-3) / 1e9)
+    # Cold-cache kernel times: reading a 1 GiB buffer between steps (outside the
+    # events) leaves L2 and the 256 MB MALL holding only clean lines of that buffer.
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    cold_order = cycle(nsteps, 20)
+    cold = np.array(time_each([lambda t=t: dev.step_fused(t) for t in cold_order], torch,
+                              flush=lambda: scratch.sum()))
+    cb = np.array([decode_bytes(case.steps[t], sh)[0] for t in cold_order]) + sb
+    out["c3_fused_cold_us_mean"] = float(cold.mean() * 1e3)
+    out["c3_fused_cold_gbs"] = float(cb.sum() / (cold.sum() * 1e-3) / 1e9)
+    del scratch
+    return out
+
+
+# ---------------------------------------------------------------------------
+# other workloads (extras)
+# ---------------------------------------------------------------------------
 
 def extra_decode(name, torch, reps=50, tp=1):
     """Decode alone on a fresh pool, timed after 50 ms of warm launches.  ``tp`` > 1 runs
@@ -243,8 +307,7 @@ def extra_block_size(bs, torch, tp=1):
     dev = DeviceDecode(case, poison=False)
     nst = len(case.steps)
     sh = case.shape
-    store_bytes = 2 * 2 * case.batch * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * case.batch
-    alg = np.array([decode_bytes(st, sh)[0] for st in case.steps]) + store_bytes
+    alg = np.array([decode_bytes(st, sh)[0] for st in case.steps]) + store_bytes(sh, case.batch)
     for t in range(nst):
         dev.step_fused(t)
     state = {"t": 0}
@@ -303,7 +366,6 @@ def extra_block_manager():
     U[100, 1024] tokens (30 % sharing a 512-token stem) allocated in one prefill step,
     then 50 decode steps, each appending one token per sequence and writing the step's
     block tables, lengths and slots (block size 256, 2048 blocks)."""
-    import time
     from paged_kv_cache_319_amd import BlockManager, _native
     rng = np.random.default_rng(1003)
     stem = rng.integers(0, 32000, size=512)
@@ -338,28 +400,30 @@ def extra_block_manager():
             "block_manager_decode_step_us": float((t3 - t2) / 50 * 1e6)}
 
 
+def prefill_flops(case):
+    sh = case.shape
+    n = case.num_new.astype(np.float64)
+    p = case.num_cached.astype(np.float64)
+    return 4.0 * sh.head_dim * sh.num_q_heads * float(np.sum(n * p + n * (n + 1) / 2))
+
+
 def extra_prefill(torch, reps=20, bs=None):
     from workloads import prefill_config
     from paged_kv_cache_319_amd.harness import DevicePrefill
     case = prefill_config(block_size=bs)
     tag = "c5" if bs is None else f"c5_bs{bs}"
-    try:
-        dev = DevicePrefill(case, poison=True)
-        dev.store()
-        dev.attend()
-    except Exception as e:  # prefill not available: report, do not fail the bench
-        return {f"{tag}_prefill_error": str(e)}
-    sh = case.shape
-    n = case.num_new.astype(np.float64)
-    p = case.num_cached.astype(np.float64)
-    flops = 4.0 * sh.head_dim * sh.num_q_heads * float(np.sum(n * p + n * (n + 1) / 2))
+    dev = DevicePrefill(case, poison=True)
     dev.store()
+    dev.attend()
+    sh = case.shape
+    flops = prefill_flops(case)
     warm(dev.attend, torch)
     store = dev.prepare_store()                 # arguments marshalled once: kernel-bound
     st = time_region(store, reps, torch)        # the store is idempotent
     at = time_region(dev.attend, reps, torch)
-    rows = int(case.k_new.shape[0])
-    sbytes = 2 * 2 * int(n.sum()) * sh.num_kv_heads * sh.head_dim * sh.elem_bytes + 4 * rows
+    # the real rows are moved; every row, padding included, has a slot to read
+    sbytes = 2 * 2 * int(case.num_new.sum()) * sh.num_kv_heads * sh.head_dim * sh.elem_bytes \
+        + 4 * int(case.k_new.shape[0])
     out = {f"{tag}_prefill_us": float(at * 1e3),
            f"{tag}_prefill_tflops": float(flops / (at * 1e-3) / 1e12),
            f"{tag}_prefill_mfma_frac": float(flops / (at * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS),
@@ -393,17 +457,7 @@ def extra_sampler(torch, reps=50, dtype="bf16"):
     # partly read cached lines.  Cold: a 1 GiB read between launches (outside the
     # events); the HBM fraction is taken from this median.
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    ev = []
-    for _ in range(30):
-        scratch.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        dev.sample()
-        e1.record(stream)
-        ev.append((e0, e1))
-    torch.cuda.synchronize()
-    cold = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    cold = float(np.median(time_each([dev.sample] * 30, torch, flush=lambda: scratch.sum())))
     del scratch
     tag = "sampler" if dtype == "bf16" else f"sampler_{dtype}"
     out = {f"{tag}_us": float(ms * 1e3), f"{tag}_gbs": float(b / (ms * 1e-3) / 1e9),
@@ -467,50 +521,85 @@ def recorded_traffic():
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the float64 oracle on a bounded sample of the same workload
+# CPU baseline: the float64 oracle on the same workload, over the host's cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(case, budget_s=12.0):
-    import contextlib
+_CPU = {}   # state the forked workers inherit: the workload and the oracle's pools
+
+
+def _oracle_decode_share(pairs):
+    """Worker: the oracle's decode of each (step, sequence) pair, BLAS on one thread."""
     import oracle
-    from workloads import np_storage_dtype, poison_bits
     try:
         from threadpoolctl import threadpool_limits
         limit = threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
-        limit = contextlib.nullcontext()
+        limit = None
+    case, kc, vc = _CPU["case"], _CPU["kc"], _CPU["vc"]
+    scale = case.shape.scale
+    t0 = time.perf_counter()
+    for t, b in pairs:
+        st = case.steps[t]
+        oracle.paged_decode(st.q[b:b + 1], kc, vc, st.block_tables[b:b + 1],
+                            st.context_lens[b:b + 1], scale)
+    el = time.perf_counter() - t0
+    if limit is not None:
+        limit.restore_original_limits()
+    return len(pairs), el
+
+
+def cpu_worker_count():
+    return max(1, min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
+
+
+def cpu_baseline(case, workers=None, steps=None):
+    """The float64 oracle, unchanged, on the headline workload: the stores of the steps'
+    new rows (one process), then every (step, sequence) decode fanned out over a pool of
+    forked worker processes, one per available host core (BLAS limited to one thread
+    each).  Decoding step t reads positions below its own length only, so storing every
+    step's rows first leaves each decode's inputs as they are at its step.  Must run
+    before this process touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    import oracle
+    from workloads import np_storage_dtype, poison_bits
     sh = case.shape
-    with limit:
-        kc = oracle.new_pool(sh.num_blocks, sh.block_size, sh.num_kv_heads, sh.head_dim,
-                             np_storage_dtype(sh.dtype), poison_bits(sh.dtype))
-        vc = kc.copy()
-        f = case.fill
-        oracle.store_kvcache(kc, vc, f.k, f.v,
-                             oracle.fill_slot_mapping(f.block_tables, f.start, f.end,
-                                                      sh.block_size))
-        # time store + decode of the workload's steps in order, sequence by sequence,
-        # until the budget is spent
-        t0 = time.perf_counter()
-        done = 0
-        steps_done = 0
-        for st in case.steps:
-            slots, _ = oracle.decode_slot_mapping(st.block_tables, st.context_lens,
-                                                  sh.block_size)
-            oracle.store_kvcache(kc, vc, st.k_new, st.v_new, slots)
-            for b in range(case.batch):
-                oracle.paged_decode(st.q[b:b + 1], kc, vc, st.block_tables[b:b + 1],
-                                    st.context_lens[b:b + 1], sh.scale)
-                done += 1
-            steps_done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        el = time.perf_counter() - t0
-    alg = sum(decode_bytes(st, sh)[0] for st in case.steps[:steps_done])
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"store + decode of the first {steps_done} of {len(case.steps)} steps "
-                      f"of the batch-256 workload ({done} decoded tokens), numpy float64, "
-                      f"BLAS limited to 1 thread, {el:.1f} s",
+    nsteps = len(case.steps) if steps is None else min(steps, len(case.steps))
+    workers = cpu_worker_count() if workers is None else workers
+    kc = oracle.new_pool(sh.num_blocks, sh.block_size, sh.num_kv_heads, sh.head_dim,
+                         np_storage_dtype(sh.dtype), poison_bits(sh.dtype))
+    vc = kc.copy()
+    f = case.fill
+    oracle.store_kvcache(kc, vc, f.k, f.v,
+                         oracle.fill_slot_mapping(f.block_tables, f.start, f.end, sh.block_size))
+    t0 = time.perf_counter()
+    for st in case.steps[:nsteps]:
+        slots, _ = oracle.decode_slot_mapping(st.block_tables, st.context_lens, sh.block_size)
+        oracle.store_kvcache(kc, vc, st.k_new, st.v_new, slots)
+    t_store = time.perf_counter() - t0
+    pairs = [(t, b) for t in range(nsteps) for b in range(case.batch)]
+    nchunks = workers * 8
+    chunks = [pairs[i::nchunks] for i in range(nchunks) if pairs[i::nchunks]]
+    _CPU.update(case=case, kc=kc, vc=vc)
+    try:
+        with mp.get_context("fork").Pool(workers) as pool:
+            pool.map(int, range(workers))          # workers started before the clock
+            t1 = time.perf_counter()
+            res = pool.map(_oracle_decode_share, chunks, chunksize=1)
+            t_decode = time.perf_counter() - t1
+    finally:
+        _CPU.clear()
+    done = sum(n for n, _ in res)
+    cpu_s = sum(e for _, e in res) + t_store
+    el = t_store + t_decode
+    alg = sum(decode_bytes(st, sh)[0] for st in case.steps[:nsteps]) \
+        + nsteps * store_bytes(sh, case.batch)
+    return {"value": done / el, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"store + decode of all {nsteps} steps of the batch-256 workload "
+                      f"({done} decoded tokens), numpy float64, decodes spread over "
+                      f"{workers} worker processes with one BLAS thread each; "
+                      f"{el:.2f} s wall, {cpu_s:.1f} s of CPU work",
             "gbs": alg / el / 1e9,
+            "wall_s": el, "cpu_s": cpu_s,
             "cpu_model": cpu_model(),
             "host_cores_available": len(os.sched_getaffinity(0))}
 
@@ -526,6 +615,14 @@ def cpu_model():
     return None
 
 
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -533,58 +630,59 @@ def main():
                                    "design note only); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    from paged_kv_cache_319_amd._native import LIB_PATH
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first")
+    headline_run = args.only in (None, "c3")
+    case = None
+    cpu = None
+    if headline_run:
+        from workloads import decode_config
+        log("building the batch-256 workload")
+        case = decode_config("C3")
+        if not args.no_cpu and args.only is None:
+            # Before the GPU is touched: the oracle's workers are forked from this process.
+            log(f"cpu baseline (oracle) on {cpu_worker_count()} worker processes")
+            cpu = cpu_baseline(case)
     import torch
     from paged_kv_cache_319_amd import load_library
     load_library()                                    # fails loudly if not built
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(3)
-    if args.only == "copy":
-        print(json.dumps(copy_calibration(torch)), flush=True)
+    single = {"copy": lambda: copy_calibration(torch), "c5": lambda: extra_prefill(torch),
+              "sampler": lambda: extra_sampler(torch), "c4": lambda: extra_decode("C4", torch),
+              "small": lambda: extra_small_step(torch)}
+    if args.only in single:
+        print(json.dumps(single[args.only]()), flush=True)
         return
-    if args.only == "c5":
-        print(json.dumps(extra_prefill(torch)), flush=True)
-        return
-    if args.only == "sampler":
-        print(json.dumps(extra_sampler(torch)), flush=True)
-        return
-    if args.only == "c4":
-        print(json.dumps(extra_decode("C4", torch)), flush=True)
-        return
-    if args.only == "small":
-        print(json.dumps(extra_small_step(torch)), flush=True)
-        return
+
+    from paged_kv_cache_319_amd.harness import DeviceDecode
     extra = {}
-    print(f"[bench] headline workload: {args.warmup} warmup + {args.steps} timed steps",
-          file=sys.stderr, flush=True)
-    case, res = headline(args, torch, extra)
+    dev = DeviceDecode(case, poison=True)
+    log(f"headline: >= {args.warmup} warm-up steps and >= {WARMUP_FLOOR_S * 1e3:.0f} ms, "
+        f"then {args.steps} timed steps")
+    res = headline(args, torch, extra, case, dev)
     if not args.no_extra and args.only is None:
-        for name in ("C2", "C4"):
-            print(f"[bench] extra decode {name}", file=sys.stderr, flush=True)
-            extra.update(extra_decode(name, torch))
-        print("[bench] extra prefill C5", file=sys.stderr, flush=True)
-        extra.update(extra_prefill(torch))
-        for bs in (16, 64):
-            print(f"[bench] extra block size {bs}", file=sys.stderr, flush=True)
-            extra.update(extra_block_size(bs, torch))
-        extra.update(extra_prefill(torch, bs=16))
-        print("[bench] extra head shards", file=sys.stderr, flush=True)
-        extra.update(extra_block_size(None, torch, tp=2))
-        extra.update(extra_decode("C4", torch, tp=2))
-        print("[bench] extra small step", file=sys.stderr, flush=True)
-        extra.update(extra_small_step(torch))
-        print("[bench] extra sampler", file=sys.stderr, flush=True)
-        extra.update(extra_sampler(torch))
-        extra.update(extra_sampler(torch, dtype="f32"))
-        extra.update(extra_block_manager())
-    extra.update({k: res[k] for k in ("kernel_us_mean", "per_launch_event_us_p10",
-                                      "per_launch_event_us_p50", "per_launch_event_us_p90",
-                                      "effective_kv_gbs", "tflops", "kernel_tokens_per_s",
-                                      "alg_bytes_per_launch")})
-    cpu = None
-    if not args.no_cpu and args.only is None:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(case)
+        log("extra: batch-256 step as graph replays, separate launches, cold cache")
+        guarded(extra, "c3_forms", extra_c3, torch, case, dev)
+    del dev
+    torch.cuda.empty_cache()
+    if not args.no_extra and args.only is None:
+        legs = [("c2", extra_decode, ("C2", torch)), ("c4", extra_decode, ("C4", torch)),
+                ("c5", extra_prefill, (torch,)),
+                ("c3_bs16", extra_block_size, (16, torch)),
+                ("c3_bs64", extra_block_size, (64, torch)),
+                ("c5_bs16", lambda t: extra_prefill(t, bs=16), (torch,)),
+                ("c3_tp2", lambda t: extra_block_size(None, t, tp=2), (torch,)),
+                ("c4_tp2", lambda t: extra_decode("C4", t, tp=2), (torch,)),
+                ("c1_small", extra_small_step, (torch,)),
+                ("sampler", extra_sampler, (torch,)),
+                ("sampler_f32", lambda t: extra_sampler(t, dtype="f32"), (torch,)),
+                ("block_manager", extra_block_manager, ())]
+        for name, fn, a in legs:
+            log(f"extra: {name}")
+            guarded(extra, name, fn, *a)
     sh = case.shape
     line = {
         "metric": "paged-decode KV-read GB/s + decode tokens/s at batch 256; % of HBM peak",
@@ -593,6 +691,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps": res["warmup_steps"],
+        "warmup_ms": res["warmup_ms"],
         "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
@@ -609,8 +709,7 @@ def main():
         "pct_hbm_peak": res["gbs"] / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": res["gbs"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": res["gbs"] / HBM_PEAK_GBS,
-                     "traffic": recorded_traffic(),
-                     "kernel": "paged_decode_kernel<BF16,128,2,4,fast,store,2>"},
+                     "traffic": recorded_traffic(), "kernel": DECODE_KERNEL},
         "cpu_baseline": cpu,
         "extra": extra,
     }

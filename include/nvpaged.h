@@ -32,9 +32,12 @@
  *     num_q_heads a multiple of num_kv_heads with at most 8 query heads per KV head.
  *   - Every pointer is caller-owned.  Device pointers must be device memory (for
  *     example from a PyTorch tensor); host pointers are ordinary host memory.
- *     The entry points of this header keep no state between calls and allocate
- *     no memory.  (The host-side block manager of nvpaged_blocks.h keeps its
- *     state in host memory behind a handle the caller creates and destroys.)
+ *     The entry points of this header allocate no memory and, with check mode
+ *     off, keep no state between calls.  (Check mode keeps a process-wide
+ *     switch, a per-thread message and device flags, described with
+ *     nv_set_check_mode below.  The host-side block manager of nvpaged_blocks.h
+ *     keeps its state in host memory behind a handle the caller creates and
+ *     destroys.)
  *   - GPU entry points enqueue work on `stream` (a hipStream_t; NULL = the null
  *     stream) and return without synchronising.  Host-checkable argument errors
  *     are reported before anything is enqueued; a failed launch returns
@@ -114,8 +117,7 @@ nv_status nv_store_kvcache(const void* k, const void* v,
  * ------------------------------------------------------------------------- */
 size_t nv_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
                                       int32_t num_kv_heads, int32_t head_dim,
-                                      int32_t max_context_len, int32_t block_size,
-                                      int32_t dtype);
+                                      int32_t max_context_len);
 
 nv_status nv_paged_decode(void* out, const void* q,
                           const void* k_cache, const void* v_cache,
@@ -236,6 +238,11 @@ nv_status nv_sample(int32_t* tokens, const void* logits, int64_t logits_row_stri
  * mode is for debugging: it costs a synchronisation per call and must not be
  * used under stream capture.  It starts on when the environment variable
  * NV_CHECK is set to anything but "0" at the first call, off otherwise.
+ * State: the validation kernels report into device-global flags shared by the
+ * whole process (one copy per GPU); a process-wide mutex serialises checked
+ * calls from the moment the flags are reset until they are read back, so checked
+ * calls from several host threads or streams run one after another.  The
+ * message is kept per host thread.
  * ------------------------------------------------------------------------- */
 
 /* Turns check mode on (non-zero) or off; returns the previous setting (0 / 1). */

@@ -118,24 +118,27 @@ def prepare_store_kvcache(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tenso
 # ---------------------------------------------------------------------------
 
 def nv_paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int,
-                                   head_dim: int, max_context_len: int, block_size: int,
-                                   dtype: int) -> int:
+                                   head_dim: int, max_context_len: int) -> int:
     return int(_native.load().nv_paged_decode_workspace_size(
-        batch, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, dtype))
+        batch, num_q_heads, num_kv_heads, head_dim, max_context_len))
 
 
 _ws_cache = {}
 
 
-def decode_workspace(device, nbytes: int) -> Optional[torch.Tensor]:
-    """A decode workspace of at least nbytes, cached per device and reused by later
-    calls (which must be ordered on one stream)."""
+def decode_workspace(device, nbytes: int, stream=None) -> Optional[torch.Tensor]:
+    """A scratch buffer of at least nbytes for calls enqueued on ``stream`` (default: the
+    device's current stream), cached per (device, stream) and reused by later calls on
+    that stream, which the stream orders.  Calls on different streams get different
+    buffers.  A call that needs more replaces the cached buffer; a prepared call keeps the
+    buffer it was prepared with."""
     if nbytes == 0:
         return None
-    key = torch.device(device)
+    dev = torch.device(device)
+    key = (dev, _stream(stream, dev))
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(nbytes, dtype=torch.uint8, device=key)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf
 
@@ -153,8 +156,8 @@ def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
     if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
         raise ValueError("schedule must be int32 with one entry per sequence")
     if workspace is None:   # the library checks the size of a caller-provided workspace
-        need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
-        workspace = decode_workspace(k_cache.device, need)
+        need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len)
+        workspace = decode_workspace(k_cache.device, need, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = _native.load().nv_paged_decode(
@@ -170,7 +173,8 @@ def nv_paged_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
 def _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
                        context_lens, max_context_len, softmax_scale, workspace, stream,
                        schedule):
-    """Validate and marshal the fused store + decode arguments: (C function, args)."""
+    """Validate and marshal the fused store + decode arguments: (C function, args, the
+    workspace tensor the arguments point into, or None)."""
     nb, bs, hkv, d = k_cache.shape
     batch, hq = q.shape[0], q.shape[1]
     dt = _dtype_code(k_cache)
@@ -184,8 +188,8 @@ def _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, blo
     if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
         raise ValueError("schedule must be int32 with one entry per sequence")
     if workspace is None:   # the library checks the size of a caller-provided workspace
-        need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len, bs, dt)
-        workspace = decode_workspace(k_cache.device, need)
+        need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len)
+        workspace = decode_workspace(k_cache.device, need, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (
@@ -197,7 +201,7 @@ def _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, blo
         _dev(schedule, "schedule") if schedule is not None else None,
         max_context_len, batch, hq, hkv, d, nb, bs, float(softmax_scale), dt, ws_ptr, ws_len,
         _stream(stream, q.device))
-    return _native.load().nv_paged_decode_store, args
+    return _native.load().nv_paged_decode_store, args, workspace
 
 
 def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
@@ -207,9 +211,9 @@ def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tenso
                           softmax_scale: float, workspace: Optional[torch.Tensor] = None,
                           stream=None, schedule: Optional[torch.Tensor] = None) -> None:
     """Store this step's K/V rows and decode, fused into one launch."""
-    fn, args = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
-                                  block_tables, context_lens, max_context_len, softmax_scale,
-                                  workspace, stream, schedule)
+    fn, args, _ = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                     block_tables, context_lens, max_context_len, softmax_scale,
+                                     workspace, stream, schedule)
     _check("nv_paged_decode_store", fn(*args))
 
 
@@ -223,12 +227,14 @@ def prepare_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.
     """nv_paged_decode_store with its arguments validated and marshalled once: returns a
     callable that enqueues the same launch again (for steps whose buffers are fixed and
     refilled in place, where per-call marshalling would dominate a small step).  The
-    callable keeps the tensors alive; the stream is the one current at preparation."""
-    fn, args = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
-                                  block_tables, context_lens, max_context_len, softmax_scale,
-                                  workspace, stream, schedule)
+    callable keeps the tensors alive, including the workspace its arguments point into
+    (the cached one when ``workspace`` is None, even after the cache moves on to a larger
+    buffer); the stream is the one current at preparation."""
+    fn, args, ws_used = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache,
+                                           v_cache, block_tables, context_lens, max_context_len,
+                                           softmax_scale, workspace, stream, schedule)
     keep = (out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
-            workspace, schedule)
+            ws_used, schedule)
     return _prepared("nv_paged_decode_store", fn, args, keep)
 
 
@@ -281,7 +287,7 @@ def nv_sample(tokens: torch.Tensor, logits: torch.Tensor, temperatures: torch.Te
               stream=None) -> None:
     """tokens: int32 [B] (device); logits: [B, V] float32 or bfloat16 (rows may be
     strided); temperatures: float32 [B]; gumbel: float32 [B, V] (rows may be strided).
-    Without ``workspace`` a cached per-device buffer is used."""
+    Without ``workspace`` the buffer cached for the device and stream is used."""
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be [B, V] with contiguous rows")
     B, V = logits.shape
@@ -293,7 +299,7 @@ def nv_sample(tokens: torch.Tensor, logits: torch.Tensor, temperatures: torch.Te
         raise ValueError("tokens must be int32 with one entry per row")
     need = nv_sample_workspace_size(B, V)
     if workspace is None:
-        workspace = decode_workspace(logits.device, need)
+        workspace = decode_workspace(logits.device, need, stream)
     ws_ptr = 0 if workspace is None else _dev(workspace, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _native.load().nv_sample(

@@ -227,14 +227,23 @@ bool check_enabled() {
 
 unsigned grid_for(int64_t n) { return static_cast<unsigned>((n + kThreads - 1) / kThreads); }
 
-// Clears the flag, runs `launch` on the stream, waits, and reads the flag back.
+// Resets the process-wide check state on the stream: no violation found yet and, for a
+// prefill check with a tile schedule, no tiles counted yet.
+__global__ void reset_check_state_kernel(bool tiles) {
+  if (threadIdx.x == 0) {
+    g_first_violation = ~0ull;
+    if (tiles) g_tile_total = 0;
+  }
+}
+
+// Under the process-wide lock (the device flags are shared by every check of the
+// process): resets the flags, runs `launch` on the stream, waits, and reads the first
+// violation back.
 template <typename F>
-nv_status run_check(const char* what, hipStream_t s, F launch) {
+nv_status run_check(const char* what, hipStream_t s, bool reset_tiles, F launch) {
   std::lock_guard<std::mutex> lock(g_check_mutex);
   const unsigned long long none = ~0ull;
-  if (hipMemcpyToSymbolAsync(HIP_SYMBOL(g_first_violation), &none, sizeof(none), 0,
-                             hipMemcpyHostToDevice, s) != hipSuccess)
-    return NV_ERR_HIP;
+  reset_check_state_kernel<<<1, 64, 0, s>>>(reset_tiles);
   launch();
   if (hipGetLastError() != hipSuccess) return NV_ERR_HIP;
   unsigned long long first = none;
@@ -262,7 +271,7 @@ nv_status store(const int32_t* slots, int32_t n, int32_t num_blocks, int32_t blo
                 void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t limit = static_cast<int64_t>(num_blocks) * block_size;
-  return run_check("nv_store_kvcache", s, [&] {
+  return run_check("nv_store_kvcache", s, false, [&] {
     check_slots_kernel<<<grid_for(n), kThreads, 0, s>>>(slots, n, limit, n <= kMaxPairwise);
   });
 }
@@ -272,7 +281,7 @@ nv_status decode(const int32_t* tables, int32_t width, const int32_t* lens,
                  int32_t block_size, int32_t num_blocks, int32_t max_len, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t limit = static_cast<int64_t>(num_blocks) * block_size;
-  return run_check(new_slots ? "nv_paged_decode_store" : "nv_paged_decode", s, [&] {
+  return run_check(new_slots ? "nv_paged_decode_store" : "nv_paged_decode", s, false, [&] {
     check_decode_kernel<<<grid_for(batch), kThreads, 0, s>>>(tables, width, lens, schedule,
                                                              new_slots, batch, block_size,
                                                              num_blocks, max_len,
@@ -289,11 +298,7 @@ nv_status prefill(const int32_t* cu_q, const int32_t* cu_k, const int32_t* table
                   void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool with_tiles = tiles && num_tiles > 0;
-  const unsigned long long zero = 0;
-  if (with_tiles && hipMemcpyToSymbolAsync(HIP_SYMBOL(g_tile_total), &zero, sizeof(zero), 0,
-                                           hipMemcpyHostToDevice, s) != hipSuccess)
-    return NV_ERR_HIP;
-  return run_check("nv_paged_prefill", s, [&] {
+  return run_check("nv_paged_prefill", s, with_tiles, [&] {
     check_prefill_kernel<<<grid_for(num_seqs), kThreads, 0, s>>>(
         cu_q, cu_k, tables, width, num_seqs, block_size, num_blocks, max_q, max_k,
         with_tiles ? tile_rows : 0);
@@ -307,7 +312,7 @@ nv_status prefill(const int32_t* cu_q, const int32_t* cu_k, const int32_t* table
 
 nv_status sample(const float* temperatures, int32_t batch, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return run_check("nv_sample", s, [&] {
+  return run_check("nv_sample", s, false, [&] {
     check_temperatures_kernel<<<grid_for(batch), kThreads, 0, s>>>(temperatures, batch);
   });
 }

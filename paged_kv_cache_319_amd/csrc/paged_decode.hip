@@ -11,7 +11,7 @@
 // Work decomposition.  A work item is (KV head j, sequence b, chunk c): tokens
 // [c*chunk, (c+1)*chunk) of sequence b.  The host picks the chunk: whole
 // sequences when batch * kv_heads alone fills the chip, otherwise a length
-// that yields roughly 1024 items (at least two chunks per sequence).
+// that yields roughly 512 items (at least two chunks per sequence).
 // Sequences are visited in the order of an optional schedule (the host's
 // length-descending order from nv_prepare_decode), so the longest items start
 // first and the short ones fill the tail.  The NW waves of a KV head walk its
@@ -460,10 +460,7 @@ nv_status dispatch_group(const DecodeArgs& a, int g, int batch, hipStream_t s) {
 
 extern "C" size_t nv_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
                                                  int32_t num_kv_heads, int32_t head_dim,
-                                                 int32_t max_context_len, int32_t block_size,
-                                                 int32_t dtype) {
-  (void)block_size;
-  (void)dtype;
+                                                 int32_t max_context_len) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
   return make_plan(batch, num_q_heads, num_kv_heads, head_dim, max_context_len).total;
 }

@@ -89,7 +89,7 @@ class DeviceDecode:
         self.out = torch.empty((B, sh.num_q_heads, sh.head_dim), dtype=TORCH_DTYPE[sh.dtype],
                                device=self.device)
         ws = nv_paged_decode_workspace_size(B, sh.num_q_heads, sh.num_kv_heads, sh.head_dim,
-                                            max(max_len, 1), sh.block_size, NV_DTYPE[sh.dtype])
+                                            max(max_len, 1))
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
 
     def store(self, t: int):

@@ -416,8 +416,7 @@ def test_decode_loose_length_bound(dtype, hq, hkv, bs, batch, width):
     dev = DeviceDecode(case)
     tight = dev.steps[0]["max_len"]
     loose = width * bs
-    need = nv_paged_decode_workspace_size(batch, hq, hkv, sh.head_dim, loose, bs,
-                                          1 if dtype == "bf16" else 0)
+    need = nv_paged_decode_workspace_size(batch, hq, hkv, sh.head_dim, loose)
     assert need > 0
     dev.workspace = torch.empty(max(need, dev.workspace.numel()), dtype=torch.uint8,
                                 device="cuda")
@@ -473,3 +472,35 @@ def test_decode_largest_batch():
     got2 = to_host_f64(dev2.step_fused(0))
     assert np.all(np.isfinite(got2))
     assert_close(got2[seqs], want, TOL["f32"], "batch 65535 fused step")
+
+
+def test_prepared_call_keeps_its_cached_workspace():
+    """A prepared fused call made without a workspace on a split plan (batch 8, 4 KV
+    heads: sequences cut into chunks) writes its partials into the binding's cached
+    buffer.  A later decode that needs more workspace on the same stream replaces the
+    cached buffer, and new allocations overwrite the freed one; the prepared call still
+    owns its buffer and matches the oracle."""
+    from paged_kv_cache_319_amd import api
+    from paged_kv_cache_319_amd.harness import DeviceDecode, to_host_f64
+    banner("prepared call keeps its cached workspace")
+    sh = Shape("bf16", 16, 4, 128, 256, 64, 0.5)
+    case = build_decode("prep-ws", sh, [700, 1500, 300, 2000, 1024, 257, 1800, 999], seed=21)
+    dev = DeviceDecode(case)
+    s = dev.steps[0]
+    api._ws_cache.clear()
+    launch = api.prepare_paged_decode_store(dev.out, s["q"], s["k"], s["v"], s["slots"], dev.kc,
+                                            dev.vc, s["tables"], s["lens"], s["max_len"],
+                                            sh.scale)
+    need = api.nv_paged_decode_workspace_size(8, 16, 4, 128, s["max_len"])
+    assert need > 0
+    first = next(iter(api._ws_cache.values()))
+    # grow the cache: a bound of 64 blocks' tokens needs more chunks, more partials
+    bigger = api.decode_workspace("cuda:0", 64 * need)
+    assert bigger is not first
+    del first
+    junk = [torch.full((need // 4 + 64,), float("nan"), device="cuda") for _ in range(8)]
+    launch()
+    got = to_host_f64(dev.out)
+    want = OracleDecode(case).run_to(0)
+    assert_close(got, want, TOL["bf16"], "prepared call after the cache grew")
+    del junk

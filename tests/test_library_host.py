@@ -145,9 +145,9 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.nv_paged_decode(*args(W=64, maxlen=1000, wsn=1 << 30)) == -3  # null workspace
     assert lib.nv_paged_decode(*args(B=0)) == 0
     # workspace size: none when every sequence is one work item, positive when split
-    assert lib.nv_paged_decode_workspace_size(4, 16, 8, 128, 256, 256, 1) == 0
-    assert lib.nv_paged_decode_workspace_size(4, 16, 8, 128, 257, 256, 1) > 0
-    assert lib.nv_paged_decode_workspace_size(256, 16, 8, 128, 4096, 256, 1) == 0
+    assert lib.nv_paged_decode_workspace_size(4, 16, 8, 128, 256) == 0
+    assert lib.nv_paged_decode_workspace_size(4, 16, 8, 128, 257) > 0
+    assert lib.nv_paged_decode_workspace_size(256, 16, 8, 128, 4096) == 0
     # prefill: causal with bad heads, unsupported dtype, zero sequences is a no-op
     pre = lambda **kw: [p, p, p, p, p, p, 16, 16, p, 4, kw.get("S", 2), None, 0,
                         kw.get("hq", 4), 2, kw.get("d", 128), 8, 16, kw.get("sc", 0.1), 1,

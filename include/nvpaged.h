@@ -155,6 +155,40 @@ nv_status nv_paged_decode_store(void* out, const void* q,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------- *
+ * fused store + decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and launches as
+ * nv_paged_decode_store minus the workspace: the fp32 partials of split
+ * sequences go to a device array inside the library instead, one copy per GPU
+ * of NV_DECODE_STATIC_SCRATCH_BYTES bytes, set up on the first call on that GPU
+ * (with that GPU current: the stream must belong to the current device) and
+ * held until the process ends.  The call allocates nothing.  It returns
+ * NV_ERR_WORKSPACE_TOO_SMALL, before touching the GPU, when the partials would
+ * exceed that size (nv_paged_decode_workspace_size(...) > the limit); every
+ * plan with batch * num_q_heads <= 8000 fits (head_dim <= 128).  The
+ * array keeps whatever the last call left; nothing in it needs initial
+ * contents.  All calls on one GPU share the array: calls that may overlap (on
+ * different streams, or from different host threads without ordering) race
+ * and give undefined results; order them on one stream.
+ * ------------------------------------------------------------------------- */
+#define NV_DECODE_STATIC_SCRATCH_BYTES (8u << 20)
+
+nv_status nv_paged_decode_store_noalloc(void* out, const void* q,
+                                        const void* k_new, const void* v_new,
+                                        int64_t k_row_stride, int64_t v_row_stride,
+                                        const int32_t* slot_mapping,
+                                        void* k_cache, void* v_cache,
+                                        const int32_t* block_tables,
+                                        int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens,
+                                        const int32_t* schedule,
+                                        int32_t max_context_len, int32_t batch,
+                                        int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t num_blocks,
+                                        int32_t block_size, float softmax_scale,
+                                        int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------- *
  * paged varlen prefill  ([walkthrough] 七: the prefill call takes q, the cache,
  * cu_seqlens_q/k, max_seqlen_q/k, causal=True and the block table; 八: only the
  * uncached part of each sequence is computed)

@@ -8,7 +8,7 @@ ABI and raise NvError on a non-OK status.  The library must be built
 from .api import (  # noqa: F401
     NV_OK, NV_F32, NV_BF16, NvError,
     nv_status_string, nv_store_kvcache, prepare_store_kvcache, nv_paged_decode_workspace_size, nv_paged_decode,
-    nv_paged_decode_store, prepare_paged_decode_store,
+    nv_paged_decode_store, prepare_paged_decode_store, nv_paged_decode_store_noalloc,
     nv_paged_prefill, nv_paged_prefill_tile_rows, nv_prepare_decode, nv_prepare_prefill,
     decode_workspace, nv_sample_workspace_size, nv_sample, nv_set_check_mode, nv_check_message,
 )

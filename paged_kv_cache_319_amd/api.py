@@ -124,6 +124,7 @@ def nv_paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: i
 
 
 _ws_cache = {}
+_NO_WORKSPACE = object()   # marks a call that takes no workspace at all
 
 
 def decode_workspace(device, nbytes: int, stream=None) -> Optional[torch.Tensor]:
@@ -187,7 +188,9 @@ def _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, blo
             raise ValueError(f"{name} must be int32")
     if schedule is not None and (schedule.dtype != torch.int32 or schedule.numel() != batch):
         raise ValueError("schedule must be int32 with one entry per sequence")
-    if workspace is None:   # the library checks the size of a caller-provided workspace
+    if workspace is _NO_WORKSPACE:
+        workspace = None
+    elif workspace is None:   # the library checks the size of a caller-provided workspace
         need = nv_paged_decode_workspace_size(batch, hq, hkv, d, max_context_len)
         workspace = decode_workspace(k_cache.device, need, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -215,6 +218,23 @@ def nv_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tenso
                                      block_tables, context_lens, max_context_len, softmax_scale,
                                      workspace, stream, schedule)
     _check("nv_paged_decode_store", fn(*args))
+
+
+def nv_paged_decode_store_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                  v_new: torch.Tensor, slot_mapping: torch.Tensor,
+                                  k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  max_context_len: int, softmax_scale: float, stream=None,
+                                  schedule: Optional[torch.Tensor] = None) -> None:
+    """nv_paged_decode_store without a workspace: split partials go to the library's own
+    per-GPU device array, so the call allocates nothing (calls on one GPU must be ordered
+    on one stream)."""
+    fn, args, _ = _decode_store_call(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                     block_tables, context_lens, max_context_len, softmax_scale,
+                                     _NO_WORKSPACE, stream, schedule)
+    # the same arguments minus the workspace pointer and size
+    _check("nv_paged_decode_store_noalloc",
+           _native.load().nv_paged_decode_store_noalloc(*args[:-3], args[-1]))
 
 
 def prepare_paged_decode_store(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,

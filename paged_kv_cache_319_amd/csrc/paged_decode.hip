@@ -42,6 +42,7 @@
 // device-scope release/acquire fences per workgroup; on this chip each writes
 // back and invalidates a whole L2 and costs far more than the second launch.)
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -578,5 +579,63 @@ extern "C" nv_status nv_paged_decode_store(void* out, const void* q, const void*
                      schedule, max_context_len, batch, num_q_heads, num_kv_heads, head_dim,
                      num_blocks, block_size, softmax_scale, dtype, workspace, workspace_bytes,
                      stream, k_new, v_new, k_row_stride, v_row_stride,
+                     batch > 0 ? slot_mapping : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of the fused store + decode.  The split-K partials live
+// in `scratch`, a device array of this file (one copy per GPU, held until the
+// process ends) instead of a caller workspace.  Host code never passes the array's
+// name to a kernel (in host code it is only a stand-in for the symbol): the device
+// address is looked up once per GPU, with that GPU current, and kept.
+// ---------------------------------------------------------------------------
+
+static __device__ __align__(256) unsigned char scratch[NV_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the current GPU (set up on the first call there).
+nv_status scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return NV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return NV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NV_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return NV_OK;
+}
+
+}  // namespace
+
+extern "C" nv_status nv_paged_decode_store_noalloc(
+    void* out, const void* q, const void* k_new, const void* v_new, int64_t k_row_stride,
+    int64_t v_row_stride, const int32_t* slot_mapping, void* k_cache, void* v_cache,
+    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+    const int32_t* schedule, int32_t max_context_len, int32_t batch, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+    float softmax_scale, int32_t dtype, void* stream) {
+  if (batch > 0 && !slot_mapping) return NV_ERR_INVALID_ARG;
+  // Partials this call needs (0 when no sequence is split); decided before any GPU call.
+  const size_t need = nv_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                     max_context_len);
+  if (need > NV_DECODE_STATIC_SCRATCH_BYTES) return NV_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0) {
+    const nv_status st = scratch_for_current_device(&ws);
+    if (st != NV_OK) return st;
+  }
+  return decode_impl(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     schedule, max_context_len, batch, num_q_heads, num_kv_heads, head_dim,
+                     num_blocks, block_size, softmax_scale, dtype, ws,
+                     need > 0 ? static_cast<size_t>(NV_DECODE_STATIC_SCRATCH_BYTES) : 0, stream,
+                     k_new, v_new, k_row_stride, v_row_stride,
                      batch > 0 ? slot_mapping : nullptr);
 }

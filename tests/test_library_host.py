@@ -214,3 +214,21 @@ def test_prepare_prefill_tile_schedule(lib):
     c2 = build_prefill("t", sh2, [5, 0, 33], [16, 48, 0], seed=3, pad_to=8)
     t2 = nv_prepare_prefill(c2.block_tables, c2.num_cached, c2.num_new, 16, 64, 8, tile_rows=32)[5]
     assert sorted(map(tuple, t2.tolist())) == [(0, 0), (2, 0), (2, 1)]
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_array_before_any_gpu_call(lib):
+    """nv_paged_decode_store_noalloc: a split plan whose partials exceed the library's
+    8 MiB per-GPU array is refused with NV_ERR_WORKSPACE_TOO_SMALL before anything touches
+    the GPU (the pointers below are never dereferenced); the size query decides it."""
+    p = ctypes.c_void_p(256)
+    B, hq, hkv, d, maxlen = 1100, 8, 1, 128, 1024        # 1100 items: two chunks each
+    need = lib.nv_paged_decode_workspace_size(B, hq, hkv, d, maxlen)
+    assert need > 8 << 20
+    args = [p, p, p, p, hkv * d, hkv * d, p, p, p, p, 8, p, None, maxlen, B, hq, hkv, d,
+            4096, 256, 0.1, 1, None]
+    assert lib.nv_paged_decode_store_noalloc(*args) == -3
+    args[6] = None                                        # no slot_mapping
+    assert lib.nv_paged_decode_store_noalloc(*args) == -1
+    # the largest plans it takes: batch * num_q_heads up to 8000 fit
+    assert lib.nv_paged_decode_workspace_size(1000, 8, 1, 128, 1024) <= 8 << 20
+    assert lib.nv_paged_decode_store_noalloc(*(args[:14] + [0] + args[15:])) == 0   # batch 0

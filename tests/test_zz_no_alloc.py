@@ -1,0 +1,62 @@
+"""The allocation-free fused store + decode (nv_paged_decode_store_noalloc), whose split
+partials live in the library's own per-GPU device array, against the fused entry point
+with a caller workspace (nv_paged_decode_store) and the oracle, on two calls in a row,
+the second with a smaller input."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from workloads import decode_config
+from oracle_runs import OracleDecode
+from gpu_common import TOL, assert_close, banner
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from paged_kv_cache_319_amd import load_library
+    load_library()
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+
+
+def _noalloc_step(dev, t):
+    from paged_kv_cache_319_amd import nv_paged_decode_store_noalloc
+    s = dev.steps[t]
+    nv_paged_decode_store_noalloc(dev.out, s["q"], s["k"], s["v"], s["slots"], dev.kc, dev.vc,
+                                  s["tables"], s["lens"], s["max_len"], dev.case.shape.scale,
+                                  schedule=s["schedule"])
+    return dev.out
+
+
+def test_noalloc_matches_workspace_entry_point_on_two_calls():
+    """Call 1: the 32K-context decode (8 sequences of 32 768 tokens, split 8 ways).
+    Call 2: 16 sequences of the batch-64 recipe (128-4096 tokens, split 4 ways): fewer
+    partials in the same array.  Each: outputs and pool bits identical to the
+    workspace entry point's, outputs within the bf16 tolerance of the oracle."""
+    from paged_kv_cache_319_amd import nv_paged_decode_workspace_size
+    from paged_kv_cache_319_amd.harness import DeviceDecode, to_host_bits, to_host_f64
+    sizes = []
+    for name, kw, seqs in (("C4", {}, [0, 5]), ("C2", {"batch": 16}, None)):
+        banner(f"no-alloc fused decode {name} {kw}")
+        case = decode_config(name, **kw)
+        sh = case.shape
+        ref = DeviceDecode(case)
+        dev = DeviceDecode(case)
+        need = nv_paged_decode_workspace_size(case.batch, sh.num_q_heads, sh.num_kv_heads,
+                                              sh.head_dim, ref.steps[0]["max_len"])
+        assert need > 0, "the case must split sequences so that the array is used"
+        sizes.append(need)
+        want_bits = to_host_bits(ref.step_fused(0)).copy()
+        got = _noalloc_step(dev, 0)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(got), want_bits), "differs from the workspace call"
+        for p, q in ((ref.kc, dev.kc), (ref.vc, dev.vc)):
+            assert np.array_equal(to_host_bits(p).view(np.uint8), to_host_bits(q).view(np.uint8))
+        want = OracleDecode(case).run_to(0, seqs=seqs)
+        out = to_host_f64(got)
+        assert_close(out if seqs is None else out[np.asarray(seqs)], want, TOL[sh.dtype],
+                     f"no-alloc {name}")
+        del ref, dev
+        torch.cuda.empty_cache()
+    assert sizes[1] < sizes[0]

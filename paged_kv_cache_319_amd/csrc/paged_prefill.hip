@@ -160,8 +160,8 @@ template <typename DT>
 __device__ __forceinline__ void store4(typename DT::T* p, float a, float b, float c, float d);
 template <>
 __device__ __forceinline__ void store4<BF16>(uint16_t* p, float a, float b, float c, float d) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16),
-                                            f32_to_bf16_rne(c) | (f32_to_bf16_rne(d) << 16));
+  // v_cvt_pk_bf16_f32 rounds to nearest even, as the output rounding requires
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
 }
 template <>
 __device__ __forceinline__ void store4<F32>(float* p, float a, float b, float c, float d) {

@@ -634,9 +634,11 @@ def main():
                                    "design note only); --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
-    from paged_kv_cache_319_amd._native import LIB_PATH
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first")
+    # The path only (importing the package would import torch before the oracle's
+    # workers are forked); the library itself is loaded after the CPU leg.
+    lib_path = os.path.join(ROOT, "paged_kv_cache_319_amd", "libnvpaged.so")
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing: build the HIP library first")
     headline_run = args.only in (None, "c3")
     case = None
     cpu = None

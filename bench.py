@@ -48,7 +48,7 @@ def parse(argv=None):
                          "50-step workload)")
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", choices=["c3", "c4", "c5", "copy", "sampler", "small"],
+    ap.add_argument("--only", choices=["c3", "c4", "c5", "copy", "sampler", "small", "sweep"],
                     default=None,
                     help="run one leg only (for profiler runs); c3 = the headline alone")
     args = ap.parse_args(argv)
@@ -474,6 +474,53 @@ def extra_sampler(torch, reps=50, dtype="bf16"):
     return out
 
 
+def sweep(torch):
+    """Where the kernels sit across sizes: the fused decode step at batch 1 .. 1024 (the
+    batch-256 recipe: lengths U[100, 1024], 16 q / 8 kv heads, head_dim 128, block 256,
+    bf16; prepared call, back to back after 50 ms warm) and causal prefill over 2-32
+    sequences of 128 .. 8192 new tokens (32 q / 8 kv heads, no prefix) beside the
+    varlen workload with cached prefixes."""
+    from workloads import build_decode, build_prefill, prefill_config, Shape
+    from paged_kv_cache_319_amd.harness import DeviceDecode, DevicePrefill
+    out = {"decode": [], "prefill": []}
+    rng = np.random.default_rng(1234)
+    for batch in (1, 4, 16, 64, 256, 1024):
+        sh = Shape("bf16", 16, 8, 128, 256, max(64, 5 * batch), 0.5)
+        lens = rng.integers(100, 1024, endpoint=True, size=batch)
+        case = build_decode("sweep", sh, lens, seed=batch)
+        dev = DeviceDecode(case, poison=False)
+        launch = dev.prepare_fused(0)
+        warm(launch, torch)
+        ms = time_region(launch, 100, torch)
+        b = decode_bytes(case.steps[0], sh)[0] + store_bytes(sh, batch)
+        out["decode"].append({"batch": batch, "us": ms * 1e3, "gbs": b / (ms * 1e-3) / 1e9,
+                              "hbm_frac": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "tokens_per_s": batch / (ms * 1e-3)})
+        del dev, launch
+        torch.cuda.empty_cache()
+    shapes = [(32, 128), (16, 512), (8, 1024), (4, 2048), (2, 4096), (2, 8192)]
+    for seqs, n in shapes:
+        sh = Shape("bf16", 32, 8, 128, 256, seqs * (-(-n // 256)) + 8, 0.5)
+        case = build_prefill("sweep", sh, [n] * seqs, [0] * seqs, seed=n, pad_to=128)
+        out["prefill"].append(_time_prefill(torch, case, f"{seqs} x {n}"))
+    out["prefill"].append(_time_prefill(torch, prefill_config(), "varlen with cached prefixes"))
+    return {"sweep": out}
+
+
+def _time_prefill(torch, case, name):
+    from paged_kv_cache_319_amd.harness import DevicePrefill
+    dev = DevicePrefill(case, poison=False)
+    dev.store()
+    warm(dev.attend, torch)
+    ms = time_region(dev.attend, 20, torch)
+    fl = prefill_flops(case)
+    res = {"case": name, "us": ms * 1e3, "tflops": fl / (ms * 1e-3) / 1e12,
+           "mfma_frac": fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    del dev
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(torch, reps=5):
     """A plain 1 GiB device copy: known bytes for scaling the HBM traffic counters."""
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -658,7 +705,7 @@ def main():
         sys.exit(3)
     single = {"copy": lambda: copy_calibration(torch), "c5": lambda: extra_prefill(torch),
               "sampler": lambda: extra_sampler(torch), "c4": lambda: extra_decode("C4", torch),
-              "small": lambda: extra_small_step(torch)}
+              "small": lambda: extra_small_step(torch), "sweep": lambda: sweep(torch)}
     if args.only in single:
         print(json.dumps(single[args.only]()), flush=True)
         return

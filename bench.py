@@ -537,8 +537,9 @@ def copy_calibration(torch, reps=5):
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "paged_decode_c3_hbm_traffic.md")
+# the kernel and the host code that orders its work (the order shapes the cache hits)
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_319_amd", "csrc", f)
-                  for f in ("paged_decode.hip", "common.h")]
+                  for f in ("paged_decode.hip", "common.h", "prepare.cpp")]
 
 
 def decode_source_digest():

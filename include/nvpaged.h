@@ -32,8 +32,9 @@
  *     num_q_heads a multiple of num_kv_heads with at most 8 query heads per KV head.
  *   - Every pointer is caller-owned.  Device pointers must be device memory (for
  *     example from a PyTorch tensor); host pointers are ordinary host memory.
- *     The entry points of this header allocate no memory and, with check mode
- *     off, keep no state between calls.  (Check mode keeps a process-wide
+ *     The GPU entry points of this header allocate no memory (the host builders
+ *     use temporary host memory) and, with check mode off, keep no state between
+ *     calls.  (Check mode keeps a process-wide
  *     switch, a per-thread message and device flags, described with
  *     nv_set_check_mode below.  The host-side block manager of nvpaged_blocks.h
  *     keeps its state in host memory behind a handle the caller creates and
@@ -296,8 +297,11 @@ const char* nv_check_message(void);
 
 /* Decode: slot_mapping[b] = slot of position context_lens[b] - 1 (the token
  * decoded this step); *max_context_len = max_b context_lens[b] (0 if batch == 0).
- * If schedule is not NULL it receives 0..batch-1 ordered by context length,
- * longest first (ties in index order), for nv_paged_decode. */
+ * If schedule is not NULL it receives 0..batch-1 in the order nv_paged_decode
+ * should start the sequences: first those whose leading block-table entries
+ * (within their length) equal another sequence's at the same positions (a shared
+ * prefix), more such entries first, then by context length, longest first; ties
+ * in index order.  Uses temporary host memory. */
 nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_blocks_per_seq,
                             const int32_t* context_lens, int32_t batch,
                             int32_t block_size, int32_t num_blocks,

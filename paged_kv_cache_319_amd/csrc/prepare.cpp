@@ -63,10 +63,43 @@ extern "C" nv_status nv_prepare_decode(const int32_t* block_tables, int32_t max_
   }
   *max_context_len = mx;
   if (schedule) {
-    // Longest sequences first, so their work items start before the short ones.
+    // Sequences whose leading blocks other sequences of the batch hold too (a shared,
+    // ref-counted prefix at the same logical positions) come first, those with more
+    // shared leading blocks first, so that the sharers' reads of the same rows fall close
+    // together in time and hit the caches; within that, the longest first, so that long
+    // work items start before the short ones fill the tail.  Ties keep index order.
+    auto nblk = [&](int32_t b) {
+      const int32_t n = (context_lens[b] + block_size - 1) / block_size;
+      return n < max_blocks_per_seq ? n : max_blocks_per_seq;
+    };
+    auto row = [&](int32_t b) { return block_tables + static_cast<int64_t>(b) * max_blocks_per_seq; };
+    // Common leading entries of two rows (entries outside [0, num_blocks) never match).
+    auto common = [&](int32_t x, int32_t y) {
+      const int32_t n = std::min(nblk(x), nblk(y));
+      int32_t i = 0;
+      while (i < n && row(x)[i] == row(y)[i] && row(x)[i] >= 0 && row(x)[i] < num_blocks) ++i;
+      return i;
+    };
+    // In lexicographic order of the rows, a sequence's longest common prefix with any
+    // other sequence is with one of its neighbours.
+    std::vector<int32_t> order(batch), lead(batch, 0);
+    for (int32_t b = 0; b < batch; ++b) order[b] = b;
+    std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      const int32_t n = std::min(nblk(x), nblk(y));
+      for (int32_t i = 0; i < n; ++i)
+        if (row(x)[i] != row(y)[i]) return row(x)[i] < row(y)[i];
+      return nblk(x) != nblk(y) ? nblk(x) < nblk(y) : x < y;
+    });
+    for (int32_t k = 0; k + 1 < batch; ++k) {
+      const int32_t c = common(order[k], order[k + 1]);
+      lead[order[k]] = std::max(lead[order[k]], c);
+      lead[order[k + 1]] = std::max(lead[order[k + 1]], c);
+    }
     for (int32_t b = 0; b < batch; ++b) schedule[b] = b;
-    std::stable_sort(schedule, schedule + batch,
-                     [context_lens](int32_t x, int32_t y) { return context_lens[x] > context_lens[y]; });
+    std::stable_sort(schedule, schedule + batch, [&](int32_t x, int32_t y) {
+      if (lead[x] != lead[y]) return lead[x] > lead[y];
+      return context_lens[x] > context_lens[y];
+    });
   }
   return NV_OK;
 }

@@ -179,19 +179,34 @@ def test_gpu_entry_points_reject_bad_arguments_before_launch(lib):
     assert lib.nv_sample(*smp(B=0)) == 0
 
 
-def test_prepare_decode_schedule_is_length_descending(lib):
+@pytest.mark.parametrize("name,kw", [("C3", dict(batch=40, steps=2, num_blocks=400)),
+                                     ("C3", dict(batch=40, steps=2, num_blocks=2000, block_size=64)),
+                                     ("C2", dict(batch=24))])
+def test_prepare_decode_schedule_order(lib, name, kw):
+    """The decode schedule: sequences holding a shared prefix (leading table entries equal
+    to another sequence's at the same positions) first, more shared entries first, then
+    longest first, ties in index order; checked against a brute force over all pairs."""
     from paged_kv_cache_319_amd import nv_prepare_decode
-    case = decode_config("C3", batch=40, steps=2, num_blocks=400)
-    st = case.steps[1]
-    slots, sched, mx = nv_prepare_decode(st.block_tables, st.context_lens, 256, 400,
-                                         with_schedule=True)
-    assert sorted(sched.tolist()) == list(range(40))
-    lens = st.context_lens[sched]
-    assert np.all(np.diff(lens) <= 0)
-    # ties keep index order
-    for a, b in zip(sched[:-1], sched[1:]):
-        if st.context_lens[a] == st.context_lens[b]:
-            assert a < b
+    case = decode_config(name, **kw)
+    sh = case.shape
+    st = case.steps[-1]
+    slots, sched, mx = nv_prepare_decode(st.block_tables, st.context_lens, sh.block_size,
+                                         sh.num_blocks, with_schedule=True)
+    B = len(st.context_lens)
+    nblk = [min(-(-int(L) // sh.block_size), st.block_tables.shape[1]) for L in st.context_lens]
+    lead = [0] * B
+    for x in range(B):
+        for y in range(B):
+            if x == y:
+                continue
+            i = 0
+            while (i < min(nblk[x], nblk[y]) and st.block_tables[x, i] == st.block_tables[y, i]
+                   and 0 <= st.block_tables[x, i] < sh.num_blocks):
+                i += 1
+            lead[x] = max(lead[x], i)
+    want = sorted(range(B), key=lambda b: (-lead[b], -int(st.context_lens[b]), b))
+    assert sched.tolist() == want
+    assert (name != "C3") or max(lead) >= 1          # the workload has sharers
     assert mx == int(st.context_lens.max())
 
 

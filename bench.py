@@ -34,7 +34,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 WARMUP_FLOOR_S = 0.1           # least wall time of warm-up steps before the timed region
-MAX_CPU_WORKERS = 16           # the GPU machine's host-CPU share per GPU
+MAX_CPU_WORKERS = 16           # host cores a one-GPU share of the machine provides
 DECODE_KERNEL = "paged_decode_kernel<BF16,128,2,4,fast,store,2>"
 
 

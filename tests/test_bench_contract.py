@@ -38,7 +38,7 @@ def test_decode_bytes_counts_shared_rows_once():
 
 # ---------------------------------------------------------------------------
 # The headline flow and the batch-256 extra legs, driven with a stand-in device and a
-# stand-in torch (no GPU): every --steps value the driver may pass runs to the end,
+# stand-in torch (no GPU): every --steps value a caller may pass runs to the end,
 # times exactly that many launches from step 0 and loses no leg.
 # ---------------------------------------------------------------------------
 

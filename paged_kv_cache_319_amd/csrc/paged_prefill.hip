@@ -17,7 +17,8 @@
 // the next tile's global loads and LDS writes overlap this tile's MFMA work with
 // one barrier per tile; two waves per SIMD hide each other's softmax and LDS
 // latency.  A wave skips tiles that its causal rows cannot see and masks only
-// the tiles that cross its diagonal.
+// the tiles that cross its diagonal.  bf16 output rows are written through the
+// then idle tile buffers so that every store covers whole rows.
 //
 // Per wave and tile, with v_mfma_f32_32x32x16_bf16 (eight v_mfma_f32_32x32x2f32
 // for fp32 data):
@@ -283,6 +284,10 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   const T* __restrict__ kc = static_cast<const T*>(a.k_cache);
   const T* __restrict__ vc = static_cast<const T*>(a.v_cache);
   const int32_t* __restrict__ bt = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  // The table does not change while the kernel runs: read through the constant address
+  // space, its workgroup-uniform entries become scalar loads (no wait on vector memory).
+  typedef const __attribute__((address_space(4))) int32_t cint32_t;
+  const cint32_t* btc = (const cint32_t*)(bt);
   const int64_t slot_stride = static_cast<int64_t>(a.num_kv_heads) * D;
 
   // Q^T operand: query row q0 + qi, head_dim elements 16*kk + 8*hh + 0..7.  Rows past
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   auto load_tile = [&](int tile, u32x4 (&st)[UPT][4]) {
     if constexpr (BMODE == 2) {
       const int k0 = tile * BN;
-      const int blk = k0 < k_end ? bt[min(k0 >> a.bs_shift, last_entry)] : 0;
+      const int blk = k0 < k_end ? btc[min(k0 >> a.bs_shift, last_entry)] : 0;
       const int off0 = k0 < k_end ? (k0 & ((1 << a.bs_shift) - 1)) : 0;
       const T* __restrict__ base =
           src + (static_cast<int64_t>(blk) * a.block_size + off0) * slot_stride +
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
       if constexpr (BMODE == 1) {
         const int lb0 = (tile * BN) >> a.bs_shift;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ent[i] = bt[min(lb0 + i, last_entry)];
+        for (int i = 0; i < 4; ++i) ent[i] = btc[min(lb0 + i, last_entry)];
       }
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
@@ -606,7 +611,41 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   // Normalise and write.  O^T register r of tile dt is head_dim position
   // 32*dt + 8*(r/4) + 4*hh + r%4 of query q0 + qi.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (q0 + qi < n) {
+  if constexpr (TRV) {
+    // bf16 rows leave through LDS: written straight from the registers, each store
+    // instruction would cover 32 rows with 16 bytes apiece; read back row-major, it
+    // covers OROWS whole rows.  The tile buffers are free after the last barrier: waves
+    // 0-3 use K's, waves 4-7 V's, 32 rows each.  16-byte chunk c of row r sits at
+    // position c ^ (r % OCH), so neither the writes nor the reads conflict in the banks.
+    constexpr int OCH = D * DT::kBytes / 16;  // 16-byte chunks per row
+    constexpr int OROWS = 64 / OCH;           // rows per store instruction
+    static_assert(GW * PB == 8 && 4 * 32 * D <= 2 * BN * KROW && 4 * 32 * D <= 2 * VBUF,
+                  "output staging fits the tile buffers");
+    T* ob = (wave < 4 ? &ks[0][0] : &vt[0][0]) + (wave % 4) * 32 * D;
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int dt = 0; dt < DT32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int pos = (4 * dt + g4) ^ (qi % OCH);
+        store4<DT>(ob + qi * D + pos * EPC + 4 * hh, oacc[dt][4 * g4] * inv,
+                   oacc[dt][4 * g4 + 1] * inv, oacc[dt][4 * g4 + 2] * inv,
+                   oacc[dt][4 * g4 + 3] * inv);
+      }
+    // Only this wave's rows: its own LDS writes complete in order, no barrier needed.
+#pragma unroll
+    for (int i = 0; i < 32 / OROWS; ++i) {
+      const int r = i * OROWS + lane / OCH;
+      const int pos = lane % OCH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&ob[r * D + pos * EPC]);
+      if (q0 + r < n) {
+        T* op = static_cast<T*>(a.out) +
+                (static_cast<int64_t>(q_begin + q0 + r) * a.num_q_heads + head) * D +
+                (pos ^ (r % OCH)) * EPC;
+        *reinterpret_cast<u32x4*>(op) = v;
+      }
+    }
+  } else if (q0 + qi < n) {
     const float inv = 1.f / l_tot;
     T* op = static_cast<T*>(a.out) +
             (static_cast<int64_t>(q_begin + q0 + qi) * a.num_q_heads + head) * D;

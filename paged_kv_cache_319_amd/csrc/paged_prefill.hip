@@ -322,14 +322,25 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 
   // A 4-key unit never straddles a block (the block size is a multiple of 16).  Block
   // lookups are workgroup-uniform scalar loads where the block size allows (they never
-  // wait on the vector loads in flight): one block per tile (BMODE 2, whose loads then
-  // take a uniform base address and a 32-bit lane offset) or the tile's BN / block_size
-  // blocks (BMODE 1); otherwise each unit looks its block up itself.  Keys at or past
-  // k_end read a valid row instead (the tile's first, or row 0 of block 0 for a tile
-  // wholly past the end); the LDS write replaces them by zero (V must be finite there:
-  // its weight is zero), which keeps these loads in flight until then.
+  // wait on the vector loads in flight): one block per tile (BMODE 2, whose loads are
+  // buffer loads through a resource spanning the tile's rows below k_end: the hardware
+  // range check returns zeros for keys at or past k_end) or the tile's BN / block_size
+  // blocks (BMODE 1); otherwise each unit looks its block up itself.  In BMODE 0 and 1
+  // keys at or past k_end read a valid row instead (the tile's first, or row 0 of block
+  // 0 for a tile wholly past the end) and the LDS write replaces them by zero (V must be
+  // finite there: its weight is zero), which keeps these loads in flight until then.
   const int last_entry = a.max_blocks - 1;
   const int my_c = rtid % CPR;                     // unit u adds HALF * u to rtid
+  // BMODE 2: byte offsets of this thread's 16-byte pieces within a tile (constant), read
+  // through a buffer resource that spans the tile's keys below k_end only: the range
+  // check returns zeros for the rest, so no selects and no tail zeroing are needed.
+  const uint32_t row_bytes = static_cast<uint32_t>(slot_stride) * ES;
+  uint32_t voff[UPT][4];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u)
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      voff[u][x] = (4 * ((rtid + HALF * u) / CPR) + x) * row_bytes + my_c * 16;
   auto load_tile = [&](int tile, u32x4 (&st)[UPT][4]) {
     if constexpr (BMODE == 2) {
       const int k0 = tile * BN;
@@ -338,16 +349,27 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
       const T* __restrict__ base =
           src + (static_cast<int64_t>(blk) * a.block_size + off0) * slot_stride +
           static_cast<int64_t>(j) * D;
+      const int valid = min(max(k_end - k0, 0), BN);
+      // every input is workgroup-uniform; readfirstlane lets the compiler see it
+      // (readfirstlane returns int: each half goes back through uint32_t before it is
+      // widened, or a low word with bit 31 set would sign-extend into the high word)
+      const uint64_t b64 = reinterpret_cast<uint64_t>(base);
+      const uint32_t b_hi = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64 >> 32))));
+      const uint32_t b_lo = static_cast<uint32_t>(
+          __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64))));
+      const uint64_t bu = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
+      const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(valid * row_bytes));
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(bu), static_cast<short>(0), nrec, 0x00020000);
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
         const int unit = rtid + HALF * u;
         if (UNITS % HALF == 0 || unit < UNITS) {   // wave-uniform: UNITS is a multiple of 64
-          const int kg = unit / CPR;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const uint32_t o = static_cast<uint32_t>((4 * kg + x) * slot_stride + my_c * EPC);
-            st[u][x] = load16(base + (k0 + 4 * kg + x < k_end ? o : 0u));
-          }
+          for (int x = 0; x < 4; ++x)
+            st[u][x] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voff[u][x]), 0, 0));
         }
       }
     } else {
@@ -386,7 +408,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   // LDS write of a staged tile: K rows as they are; V rows as they are (bf16) or
   // transposed (fp32).  Only the tile holding k_end has keys to zero.
   auto store_tile = [&](T* buf, int tile, const u32x4 (&st)[UPT][4]) {
-    const bool tail = (tile + 1) * BN > k_end;     // workgroup-uniform
+    const bool tail = BMODE != 2 && (tile + 1) * BN > k_end;   // workgroup-uniform
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = rtid + HALF * u;

@@ -108,13 +108,6 @@ template <typename DT>
 __device__ __forceinline__ void frag_load_2x4(Frag<DT>& f, const typename DT::T* p0,
                                               const typename DT::T* p1);
 template <>
-__device__ __forceinline__ void frag_load_2x4<BF16>(Frag<BF16>& f, const uint16_t* p0,
-                                                    const uint16_t* p1) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p0);
-  const uint2 b = *reinterpret_cast<const uint2*>(p1);
-  f.v = u32x4{a.x, a.y, b.x, b.y};
-}
-template <>
 __device__ __forceinline__ void frag_load_2x4<F32>(Frag<F32>& f, const float* p0, const float* p1) {
   f.v[0] = *reinterpret_cast<const u32x4*>(p0);
   f.v[1] = *reinterpret_cast<const u32x4*>(p1);
@@ -154,7 +147,6 @@ __device__ __forceinline__ u32x4 tr_pair(const uint16_t* p0, const uint16_t* p1)
   const uint2 ub = __builtin_bit_cast(uint2, b);
   return u32x4{ua.x, ua.y, ub.x, ub.y};
 }
-__device__ __forceinline__ u32x4 tr_pair(const float*, const float*) { return u32x4{0, 0, 0, 0}; }
 
 // Four output elements (consecutive head_dim positions) -> memory.
 template <typename DT>
@@ -174,20 +166,6 @@ __device__ __forceinline__ void store4<F32>(float* p, float a, float b, float c,
 template <typename DT>
 __device__ __forceinline__ void write_vt(typename DT::T* vt, int vrow, int d0, int k0,
                                          const u32x4* r);
-template <>
-__device__ __forceinline__ void write_vt<BF16>(uint16_t* vt, int vrow, int d0, int k0,
-                                               const u32x4* r) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    // element 2m (low halves) and 2m + 1 (high halves) of each key
-    const uint32_t lo01 = (r[0][m] & 0xffffu) | (r[1][m] << 16);
-    const uint32_t lo23 = (r[2][m] & 0xffffu) | (r[3][m] << 16);
-    const uint32_t hi01 = (r[0][m] >> 16) | (r[1][m] & 0xffff0000u);
-    const uint32_t hi23 = (r[2][m] >> 16) | (r[3][m] & 0xffff0000u);
-    *reinterpret_cast<uint2*>(vt + (d0 + 2 * m) * vrow + k0) = make_uint2(lo01, lo23);
-    *reinterpret_cast<uint2*>(vt + (d0 + 2 * m + 1) * vrow + k0) = make_uint2(hi01, hi23);
-  }
-}
 template <>
 __device__ __forceinline__ void write_vt<F32>(float* vt, int vrow, int d0, int k0, const u32x4* r) {
 #pragma unroll
@@ -215,9 +193,8 @@ struct PrefillArgs {
   float scale_log2;    // |softmax_scale| * log2(e), > 0
 };
 
-// BMODE: how a tile's keys find their cache blocks.  2: power-of-two block size >= BN (a
-// tile lies in one block); 1: smaller power-of-two blocks (a tile spans BN / block_size
-// blocks); 0: any other block size (each 4-key unit looks its block up).
+// BMODE: how a staging wave finds the cache block of its keys: 1 for a power-of-two block
+// size (shift and mask), 0 for any other multiple of 16 (division).
 template <typename DT, int D, int GW, int PB, int BN, int BMODE>
 __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs a) {
   using T = typename DT::T;
@@ -241,7 +218,6 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   constexpr int UNITS = (BN / 4) * CPR;  // 4-key x 16-byte staging units per tile
   constexpr int NT = 64 * GW * PB;       // threads per workgroup
   constexpr int HALF = NT / 2;           // the first half stages K, the second V
-  constexpr int UPT = (UNITS + HALF - 1) / HALF;
   constexpr int BMW = 32 * PB;           // query positions per workgroup
 
   // Two K / V^T tile buffers: the next tile is written while this one is read.
@@ -311,130 +287,84 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
     }
   }
 
-  // Staging registers: the first half of the workgroup's waves stages K, the second
-  // half V, UPT units (4 keys x one 16-byte chunk) per thread.  Every call issues the
-  // same loads (a tile past the end reads the pool's first element), which keeps the
-  // compiler's count of loads in flight exact and its waits minimal.
+  // Staging: the first half of the workgroup's waves stages K, the second half V.  Each
+  // of a role's four waves gathers KPW consecutive keys of a tile, one unit (4 keys x one
+  // 16-byte chunk) per lane; lanes past UPW hold none.  A wave's keys start at a multiple
+  // of KPW, which divides 16, so they lie in one cache block for every block size (a
+  // multiple of 16): one workgroup-uniform table load per wave and tile (a scalar load,
+  // which never waits on the vector loads in flight), and the wave's loads are buffer
+  // loads through a resource whose range ends at k_end.  The hardware range check
+  // returns zeros for keys at or past k_end, so a tile's tail needs no selects on the
+  // load side and no zeroing on the LDS side (V must be finite there: its weight is 0).
+  static_assert(HALF == 256 && UNITS % 4 == 0 && UNITS / 4 <= 64, "four staging waves");
+  constexpr int UPW = UNITS / 4;          // units per staging wave
+  constexpr int KPW = 4 * UPW / CPR;      // keys per staging wave (16 bf16, 8 fp32)
+  static_assert(4 * KPW == BN && 16 % KPW == 0, "a staging wave's keys lie in one block");
   const bool v_role = wave >= (GW * PB) / 2;   // wave-uniform
   const int rtid = tid - (v_role ? HALF : 0);
+  const int swave = v_role ? wave - (GW * PB) / 2 : wave;   // staging wave in the role (uniform)
+  const bool s_on = (rtid & 63) < UPW;         // this lane holds a unit
+  const int my_unit = swave * UPW + (rtid & 63);
+  const int my_c = my_unit % CPR;              // the unit's 16-byte chunk of a row
+  const int my_kg = my_unit / CPR;             // the unit's first key is 4 * my_kg
   const T* __restrict__ src = v_role ? vc : kc;
-  u32x4 stA[UPT][4];
-
-  // A 4-key unit never straddles a block (the block size is a multiple of 16).  Block
-  // lookups are workgroup-uniform scalar loads where the block size allows (they never
-  // wait on the vector loads in flight): one block per tile (BMODE 2, whose loads are
-  // buffer loads through a resource spanning the tile's rows below k_end: the hardware
-  // range check returns zeros for keys at or past k_end) or the tile's BN / block_size
-  // blocks (BMODE 1); otherwise each unit looks its block up itself.  In BMODE 0 and 1
-  // keys at or past k_end read a valid row instead (the tile's first, or row 0 of block
-  // 0 for a tile wholly past the end) and the LDS write replaces them by zero (V must be
-  // finite there: its weight is zero), which keeps these loads in flight until then.
+  u32x4 stA[4];
   const int last_entry = a.max_blocks - 1;
-  const int my_c = rtid % CPR;                     // unit u adds HALF * u to rtid
-  // BMODE 2: byte offsets of this thread's 16-byte pieces within a tile (constant), read
-  // through a buffer resource that spans the tile's keys below k_end only: the range
-  // check returns zeros for the rest, so no selects and no tail zeroing are needed.
   const uint32_t row_bytes = static_cast<uint32_t>(slot_stride) * ES;
-  uint32_t voff[UPT][4];
+  uint32_t voff[4];   // byte offsets of the lane's pieces from the wave's first key
 #pragma unroll
-  for (int u = 0; u < UPT; ++u)
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-      voff[u][x] = (4 * ((rtid + HALF * u) / CPR) + x) * row_bytes + my_c * 16;
-  auto load_tile = [&](int tile, u32x4 (&st)[UPT][4]) {
-    if constexpr (BMODE == 2) {
-      const int k0 = tile * BN;
-      const int blk = k0 < k_end ? btc[min(k0 >> a.bs_shift, last_entry)] : 0;
-      const int off0 = k0 < k_end ? (k0 & ((1 << a.bs_shift) - 1)) : 0;
-      const T* __restrict__ base =
-          src + (static_cast<int64_t>(blk) * a.block_size + off0) * slot_stride +
-          static_cast<int64_t>(j) * D;
-      const int valid = min(max(k_end - k0, 0), BN);
-      // every input is workgroup-uniform; readfirstlane lets the compiler see it
-      // (readfirstlane returns int: each half goes back through uint32_t before it is
-      // widened, or a low word with bit 31 set would sign-extend into the high word)
-      const uint64_t b64 = reinterpret_cast<uint64_t>(base);
-      const uint32_t b_hi = static_cast<uint32_t>(
-          __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64 >> 32))));
-      const uint32_t b_lo = static_cast<uint32_t>(
-          __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64))));
-      const uint64_t bu = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
-      const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(valid * row_bytes));
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          reinterpret_cast<void*>(bu), static_cast<short>(0), nrec, 0x00020000);
-#pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-        const int unit = rtid + HALF * u;
-        if (UNITS % HALF == 0 || unit < UNITS) {   // wave-uniform: UNITS is a multiple of 64
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            st[u][x] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voff[u][x]), 0, 0));
-        }
+  for (int x = 0; x < 4; ++x)
+    voff[x] = (4 * my_kg + x - KPW * swave) * row_bytes + my_c * 16;
+  auto load_tile = [&](int tile, u32x4 (&st)[4]) {
+    const int kw0 = tile * BN + KPW * swave;   // the wave's first key
+    int blk = 0, off = 0;
+    if (kw0 < k_end) {
+      if constexpr (BMODE != 0) {
+        blk = btc[min(kw0 >> a.bs_shift, last_entry)];
+        off = kw0 & ((1 << a.bs_shift) - 1);
+      } else {
+        const int lb = min(kw0 / a.block_size, last_entry);
+        blk = btc[lb];
+        off = kw0 - lb * a.block_size;
       }
-    } else {
-      int ent[4] = {0, 0, 0, 0};
-      if constexpr (BMODE == 1) {
-        const int lb0 = (tile * BN) >> a.bs_shift;
+    }
+    const T* __restrict__ base =
+        src + (static_cast<int64_t>(blk) * a.block_size + off) * slot_stride +
+        static_cast<int64_t>(j) * D;
+    const int valid = min(max(k_end - kw0, 0), KPW);
+    // every input is workgroup-uniform; readfirstlane lets the compiler see it
+    // (readfirstlane returns int: each half goes back through uint32_t before it is
+    // widened, or a low word with bit 31 set would sign-extend into the high word)
+    const uint64_t b64 = reinterpret_cast<uint64_t>(base);
+    const uint32_t b_hi = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64 >> 32))));
+    const uint32_t b_lo = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64))));
+    const uint64_t bu = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
+    const int nrec = __builtin_amdgcn_readfirstlane(static_cast<int>(valid * row_bytes));
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(bu), static_cast<short>(0), nrec, 0x00020000);
+    if (s_on) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ent[i] = btc[min(lb0 + i, last_entry)];
-      }
-#pragma unroll
-      for (int u = 0; u < UPT; ++u) {
-        const int unit = rtid + HALF * u;
-        if (UNITS % HALF == 0 || unit < UNITS) {
-          const int c = unit % CPR;
-          const int kg = unit / CPR;
-          const int kp0 = tile * BN + 4 * kg;     // first of the unit's four keys
-          int blk, off;
-          if constexpr (BMODE == 1) {
-            const int i = (4 * kg) >> a.bs_shift;
-            blk = i == 0 ? ent[0] : i == 1 ? ent[1] : i == 2 ? ent[2] : ent[3];
-            off = kp0 & ((1 << a.bs_shift) - 1);
-          } else {
-            const int lb = min(kp0 / a.block_size, last_entry);
-            blk = bt[lb];
-            off = kp0 - lb * a.block_size;
-          }
-          const int64_t e0 = (static_cast<int64_t>(blk) * a.block_size + off) * slot_stride +
-                             static_cast<int64_t>(j) * D + c * EPC;
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            st[u][x] = load16(src + (kp0 + x < k_end ? e0 + x * slot_stride : 0));
-        }
-      }
+      for (int x = 0; x < 4; ++x)
+        st[x] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, static_cast<int>(voff[x]), 0, 0));
     }
   };
   // LDS write of a staged tile: K rows as they are; V rows as they are (bf16) or
-  // transposed (fp32).  Only the tile holding k_end has keys to zero.
-  auto store_tile = [&](T* buf, int tile, const u32x4 (&st)[UPT][4]) {
-    const bool tail = BMODE != 2 && (tile + 1) * BN > k_end;   // workgroup-uniform
+  // transposed (fp32).
+  auto store_tile = [&](T* buf, const u32x4 (&st)[4]) {
+    if (!s_on) return;
+    if (!v_role) {
 #pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int unit = rtid + HALF * u;
-      if (UNITS % HALF == 0 || unit < UNITS) {
-        const int c = unit % CPR;
-        const int kg = unit / CPR;
-        u32x4 x4[4];
+      for (int x = 0; x < 4; ++x)
+        *reinterpret_cast<u32x4*>(&buf[(4 * my_kg + x) * KROW + my_c * EPC]) = st[x];
+    } else if constexpr (TRV) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) x4[x] = st[u][x];
-        if (tail) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            if (tile * BN + 4 * kg + x >= k_end) x4[x] = u32x4{0, 0, 0, 0};
-        }
-        if (!v_role) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x4*>(&buf[(4 * kg + x) * KROW + c * EPC]) = x4[x];
-        } else if constexpr (TRV) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<u32x4*>(&buf[(4 * kg + x) * VROW + c * EPC]) = x4[x];
-        } else {
-          write_vt<DT>(buf, VROW, c * EPC, 4 * kg, x4);
-        }
-      }
+      for (int x = 0; x < 4; ++x)
+        *reinterpret_cast<u32x4*>(&buf[(4 * my_kg + x) * VROW + my_c * EPC]) = st[x];
+    } else {
+      write_vt<DT>(buf, VROW, my_c * EPC, 4 * my_kg, st);
     }
   };
 
@@ -593,15 +523,15 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
     // The K waves fill two buffers before the first barrier: a second staging set,
     // live only here, puts tiles 0 and 1 in flight together (one memory latency at
     // the start of the workgroup instead of two).
-    u32x4 stB[UPT][4];
+    u32x4 stB[4];
     load_tile(0, stA);
     load_tile(1, stB);
-    store_tile(ks[0], 0, stA);
+    store_tile(ks[0], stA);
     load_tile(2, stA);
-    store_tile(ks[1], 1, stB);
+    store_tile(ks[1], stB);
   } else {
     load_tile(0, stA);
-    store_tile(vt[0], 0, stA);
+    store_tile(vt[0], stA);
     load_tile(1, stA);
   }
   __syncthreads();
@@ -610,20 +540,20 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   __syncthreads();                                 // K(0) is overwritten in step 0
   for (int t = 0; t < ntiles; t += 2) {
     if (!v_role) {
-      store_tile(ks[0], t + 2, stA);
+      store_tile(ks[0], stA);
       load_tile(t + 3, stA);
     } else {
-      store_tile(vt[1], t + 1, stA);
+      store_tile(vt[1], stA);
       load_tile(t + 2, stA);
     }
     step(t, sA, sB, ks[1], vt[0]);
     __syncthreads();
     if (t + 1 >= ntiles) break;
     if (!v_role) {
-      store_tile(ks[1], t + 3, stA);
+      store_tile(ks[1], stA);
       load_tile(t + 4, stA);
     } else {
-      store_tile(vt[0], t + 2, stA);
+      store_tile(vt[0], stA);
       load_tile(t + 3, stA);
     }
     step(t + 1, sB, sA, ks[0], vt[1]);
@@ -695,9 +625,7 @@ nv_status launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, i
     if (tiles <= 0) return NV_OK;
     grid = dim3(tiles, heads_y, num_seqs);
   }
-  if (a.bs_shift >= 0 && (1 << a.bs_shift) >= BN)
-    paged_prefill_kernel<DT, D, GW, PB, BN, 2><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
-  else if (a.bs_shift >= 0)
+  if (a.bs_shift >= 0)
     paged_prefill_kernel<DT, D, GW, PB, BN, 1><<<grid, dim3(64 * GW * PB), 0, s>>>(a);
   else
     paged_prefill_kernel<DT, D, GW, PB, BN, 0><<<grid, dim3(64 * GW * PB), 0, s>>>(a);

@@ -485,7 +485,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
     const float m_ref = (t + 1) * BN > all_see ? tile_max(std::true_type{}, t, scur, alpha)
                                                : tile_max(std::false_type{}, t, scur, alpha);
     l_run *= alpha;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    if (t > 0 && __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {   // O is 0 before tile 0
 #pragma unroll
       for (int dt = 0; dt < DT32; ++dt)
 #pragma unroll

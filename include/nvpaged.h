@@ -165,14 +165,15 @@ nv_status nv_paged_decode_store(void* out, const void* q,
  * (with that GPU current: the stream must belong to the current device) and
  * held until the process ends.  The call allocates nothing.  It returns
  * NV_ERR_WORKSPACE_TOO_SMALL, before touching the GPU, when the partials would
- * exceed that size (nv_paged_decode_workspace_size(...) > the limit); every
- * plan with batch * num_q_heads <= 8000 fits (head_dim <= 128).  The
+ * exceed that size (nv_paged_decode_workspace_size(...) > the limit); no plan
+ * the kernels support reaches it (head_dim <= 128: the largest split plan's
+ * partials take 12.2 MiB, batch 1535 x 8 query heads over one KV head).  The
  * array keeps whatever the last call left; nothing in it needs initial
  * contents.  All calls on one GPU share the array: calls that may overlap (on
  * different streams, or from different host threads without ordering) race
  * and give undefined results; order them on one stream.
  * ------------------------------------------------------------------------- */
-#define NV_DECODE_STATIC_SCRATCH_BYTES (8u << 20)
+#define NV_DECODE_STATIC_SCRATCH_BYTES (16u << 20)
 
 nv_status nv_paged_decode_store_noalloc(void* out, const void* q,
                                         const void* k_new, const void* v_new,

@@ -11,7 +11,8 @@
 // Work decomposition.  A work item is (KV head j, sequence b, chunk c): tokens
 // [c*chunk, (c+1)*chunk) of sequence b.  The host picks the chunk: whole
 // sequences when batch * kv_heads alone fills the chip, otherwise a length
-// that yields roughly 512 items (at least two chunks per sequence).
+// that yields roughly 2048 items when the longest context is at most 8 K tokens and
+// 512 above (at least two chunks per sequence).
 // Sequences are visited in the order of an optional schedule (the host's
 // length-descending order from nv_prepare_decode), so the longest items start
 // first and the short ones fill the tail.  The NW waves of a KV head walk its
@@ -53,7 +54,12 @@ using namespace nvp;
 constexpr int kDecodeWaves = 4;
 constexpr int kPass = 256;                // chunk granularity (a multiple of every pass)
 constexpr int kSplitBelowItems = 1536;    // split sequences when fewer (head, sequence) items
-constexpr int kTargetSplitItems = 512;    // work items aimed at when splitting (>= 2 chunks)
+// Work items aimed at when splitting (>= 2 chunks per sequence): more, shorter chunks
+// balance ragged contexts up to 8 K tokens (batch 64 x U[128, 4096]: 1.5 % faster with
+// 2048 than with 512); at 32 K tokens the extra chunks cost more in merging (-5.8 %).
+constexpr int kTargetSplitItemsShort = 2048;
+constexpr int kTargetSplitItemsLong = 512;
+constexpr int kShortContext = 8192;
 
 struct DecodeArgs {
   void* out;
@@ -383,8 +389,10 @@ Plan make_plan(int batch, int hq, int hkv, int d, int max_context_len) {
   const int max_len = max_context_len < 1 ? 1 : max_context_len;
   const int64_t items = static_cast<int64_t>(batch) * hkv;
   int64_t per_seq = 1;  // chunks per sequence
-  if (items < kSplitBelowItems)
-    per_seq = std::max<int64_t>(2, (kTargetSplitItems + items - 1) / items);
+  if (items < kSplitBelowItems) {
+    const int64_t target = max_len <= kShortContext ? kTargetSplitItemsShort : kTargetSplitItemsLong;
+    per_seq = std::max<int64_t>(2, (target + items - 1) / items);
+  }
   int64_t chunk = (max_len + per_seq - 1) / per_seq;
   chunk = static_cast<int64_t>(round_up(static_cast<size_t>(chunk), kPass));
   p.chunk = static_cast<int>(chunk);

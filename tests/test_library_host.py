@@ -231,19 +231,28 @@ def test_prepare_prefill_tile_schedule(lib):
     assert sorted(map(tuple, t2.tolist())) == [(0, 0), (2, 0), (2, 1)]
 
 
-def test_noalloc_decode_rejects_partials_beyond_its_array_before_any_gpu_call(lib):
-    """nv_paged_decode_store_noalloc: a split plan whose partials exceed the library's
-    8 MiB per-GPU array is refused with NV_ERR_WORKSPACE_TOO_SMALL before anything touches
-    the GPU (the pointers below are never dereferenced); the size query decides it."""
+def test_noalloc_decode_array_holds_every_supported_plan(lib):
+    """nv_paged_decode_store_noalloc keeps split partials in a 16 MiB per-GPU array.  Every
+    plan the kernels support (head_dim <= 128) fits: split plans need fewer than 1536
+    (KV head, sequence) items and the largest take 12.2 MiB.  Partials beyond the array
+    are refused with NV_ERR_WORKSPACE_TOO_SMALL before anything touches the GPU (the
+    pointers below are never dereferenced); only a head_dim the kernels reject gets there."""
+    limit = 16 << 20
+    worst = 0
+    for g in (1, 2, 4, 8):
+        for hkv in (1, 2, 3, 4, 8, 16, 32):
+            top = 1535 // hkv
+            for B in sorted({1, 2, 7, 64, 255, 256, 500, 768, 1000, top - 1, top, top + 1} - {0}):
+                for L in (256, 512, 1024, 2048, 4096, 8192, 8193, 32768, 131072):
+                    worst = max(worst, lib.nv_paged_decode_workspace_size(B, g * hkv, hkv, 128, L))
+    assert 12 << 20 < worst <= limit
     p = ctypes.c_void_p(256)
-    B, hq, hkv, d, maxlen = 1100, 8, 1, 128, 1024        # 1100 items: two chunks each
-    need = lib.nv_paged_decode_workspace_size(B, hq, hkv, d, maxlen)
-    assert need > 8 << 20
+    B, hq, hkv, d, maxlen = 1535, 8, 1, 256, 512          # two chunks each, head_dim 256
+    assert lib.nv_paged_decode_workspace_size(B, hq, hkv, d, maxlen) > limit
     args = [p, p, p, p, hkv * d, hkv * d, p, p, p, p, 8, p, None, maxlen, B, hq, hkv, d,
             4096, 256, 0.1, 1, None]
     assert lib.nv_paged_decode_store_noalloc(*args) == -3
+    args[17] = 128
     args[6] = None                                        # no slot_mapping
     assert lib.nv_paged_decode_store_noalloc(*args) == -1
-    # the largest plans it takes: batch * num_q_heads up to 8000 fit
-    assert lib.nv_paged_decode_workspace_size(1000, 8, 1, 128, 1024) <= 8 << 20
     assert lib.nv_paged_decode_store_noalloc(*(args[:14] + [0] + args[15:])) == 0   # batch 0

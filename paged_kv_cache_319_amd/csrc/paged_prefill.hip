@@ -291,7 +291,7 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
   // of a role's four waves gathers KPW consecutive keys of a tile, one unit (4 keys x one
   // 16-byte chunk) per lane; lanes past UPW hold none.  A wave's keys start at a multiple
   // of KPW, which divides 16, so they lie in one cache block for every block size (a
-  // multiple of 16): one workgroup-uniform table load per wave and tile (a scalar load,
+  // multiple of 16): one wave-uniform table load per wave and tile (a scalar load,
   // which never waits on the vector loads in flight), and the wave's loads are buffer
   // loads through a resource whose range ends at k_end.  The hardware range check
   // returns zeros for keys at or past k_end, so a tile's tail needs no selects on the
@@ -332,9 +332,11 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
         src + (static_cast<int64_t>(blk) * a.block_size + off) * slot_stride +
         static_cast<int64_t>(j) * D;
     const int valid = min(max(k_end - kw0, 0), KPW);
-    // every input is workgroup-uniform; readfirstlane lets the compiler see it
-    // (readfirstlane returns int: each half goes back through uint32_t before it is
-    // widened, or a low word with bit 31 set would sign-extend into the high word)
+    // every input is wave-uniform; readfirstlane lets the compiler see it (readfirstlane
+    // returns int: each half goes back through uint32_t before it is widened, or a low
+    // word with bit 31 set would sign-extend into the high word).  Resource word 3
+    // (0x00020000): 32-bit data format, so the untyped 16-byte loads are range-checked
+    // against nrec bytes (stride 0: raw offsets).
     const uint64_t b64 = reinterpret_cast<uint64_t>(base);
     const uint32_t b_hi = static_cast<uint32_t>(
         __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b64 >> 32))));

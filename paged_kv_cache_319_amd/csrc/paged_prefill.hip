@@ -195,6 +195,18 @@ struct PrefillArgs {
 
 // BMODE: how a staging wave finds the cache block of its keys: 1 for a power-of-two block
 // size (shift and mask), 0 for any other multiple of 16 (division).
+// Lanes l and l ^ 32 combined without LDS: v_permlane32_swap of a value with itself
+// swaps the upper half of one copy with the lower half of the other, so in every lane the
+// two results hold the lane's own value and its partner's (a maximum or a sum of the pair
+// then needs no cross-lane read through LDS and no wait on the LDS counter).
+__device__ __forceinline__ void halves32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __uint_as_float(r0);
+  b = __uint_as_float(r1);
+}
+
 template <typename DT, int D, int GW, int PB, int BN, int BMODE>
 __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs a) {
   using T = typename DT::T;
@@ -424,7 +436,11 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
           sacc[kb][r] = 32 * kb + 8 * (r / 4) + (r % 4) < lim ? sacc[kb][r] : -INFINITY;
         tmax = fmaxf(tmax, sacc[kb][r]);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    {
+      float a0, a1;
+      halves32(tmax, a0, a1);
+      tmax = fmaxf(a0, a1);
+    }
     const float m_tile = tmax == -INFINITY ? -INFINITY : tmax * a.scale_log2;
     const float m_use = m_tile > m_run + 8.f ? m_tile : m_run;
     const float m_ref = m_use == -INFINITY ? 0.f : m_use;
@@ -564,7 +580,9 @@ __global__ __launch_bounds__(64 * GW * PB) void paged_prefill_kernel(PrefillArgs
 
   // Normalise and write.  O^T register r of tile dt is head_dim position
   // 32*dt + 8*(r/4) + 4*hh + r%4 of query q0 + qi.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  float l_a, l_b;
+  halves32(l_run, l_a, l_b);
+  const float l_tot = l_a + l_b;
   if constexpr (TRV) {
     // bf16 rows leave through LDS: written straight from the registers, each store
     // instruction would cover 32 rows with 16 bytes apiece; read back row-major, it

@@ -13,7 +13,8 @@
 // sequence and GW query heads that share one KV head (GW * PB = 8): wave w takes
 // head w % GW and position block w / GW.  K/V are walked in tiles of BN keys;
 // each tile is gathered through the block table once per workgroup into LDS
-// (K row-major, V transposed) and serves all eight waves.  Two LDS buffers let
+// (K row-major; V row-major and read transposed for bf16, transposed on its way
+// in for fp32) and serves all eight waves.  Two LDS buffers let
 // the next tile's global loads and LDS writes overlap this tile's MFMA work with
 // one barrier per tile; two waves per SIMD hide each other's softmax and LDS
 // latency.  A wave skips tiles that its causal rows cannot see and masks only

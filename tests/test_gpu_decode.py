@@ -130,6 +130,7 @@ EDGE_LENGTHS = [1, 2, 63, 64, 65, 255, 256, 257, 511, 512, 513, 767, 1024, 1025,
     ("bf16", 128, 16, 8, 256), ("bf16", 128, 8, 8, 16), ("bf16", 128, 32, 8, 16),
     ("bf16", 64, 16, 2, 32), ("bf16", 128, 64, 8, 256), ("f32", 64, 2, 1, 16),
     ("f32", 128, 8, 2, 64), ("f32", 64, 8, 1, 256), ("bf16", 128, 16, 8, 48),
+    ("bf16", 128, 16, 8, 1024), ("f32", 64, 4, 2, 272),
 ])
 def test_decode_shapes_and_chunk_edges(dtype, d, hq, hkv, bs):
     banner(f"decode edges {dtype} d{d} hq{hq} hkv{hkv} bs{bs}")

@@ -57,6 +57,7 @@ PREFILL_SHAPES = [
     ("f32", 64, 16, 2, 32), ("f32", 128, 4, 2, 64),
     ("bf16", 128, 32, 8, 256), ("bf16", 128, 16, 16, 16), ("bf16", 64, 16, 8, 32),
     ("bf16", 128, 64, 8, 16), ("bf16", 128, 16, 8, 48), ("f32", 64, 8, 2, 80),
+    ("bf16", 128, 32, 8, 1024), ("f32", 64, 8, 2, 272),
 ]
 NEW = [1, 31, 32, 33, 0, 64, 65, 100, 127, 160]
 CACHED = [0, 5, 16, 0, 7, 256, 33, 0, 48, 300]

@@ -245,8 +245,8 @@ def time_region_seq(launches, torch):
 
 def extra_c3(torch, case, dev, reps=50):
     """The headline steps in other forms, each over `reps` steps cycling from step 0:
-    replays of per-step HIP graphs, the store and the decode as separate launches, and
-    fused launches with a cold cache."""
+    replays of per-step HIP graphs, one graph holding all steps, the store and the
+    decode as separate launches, and fused launches with a cold cache."""
     sh = case.shape
     nsteps = len(case.steps)
     order = cycle(nsteps, reps)
@@ -254,6 +254,12 @@ def extra_c3(torch, case, dev, reps=50):
     dev.capture_graphs()
     out["c3_fused_graph_replay_us"] = float(
         time_region_seq([lambda t=t: dev.replay(t) for t in order], torch) * 1e3)
+    # all steps in one graph: one replay runs them back to back
+    dev.capture_sequence(range(nsteps))
+    dev.seq_graph.replay()
+    out["c3_fused_graph_seq_us"] = float(
+        time_region(lambda: dev.seq_graph.replay(), 2, torch) / nsteps * 1e3)
+    del dev.seq_graph, dev.seq_outs
     stores = {t: dev.prepare_store(t) for t in set(order)}
     st_ms = time_region_seq([stores[t] for t in order], torch)
     de_ms = time_region_seq([lambda t=t: dev.decode(t) for t in order], torch)

@@ -150,6 +150,22 @@ class DeviceDecode:
         self.graphs[t].replay()
         return self.out
 
+    def capture_sequence(self, steps):
+        """Capture the fused store + decode of several steps, in order, into ONE HIP graph
+        (one replay runs them all, so the per-launch cost of a graph is paid once);
+        step t writes its own output buffer ``self.seq_outs[t]``."""
+        sh = self.case.shape
+        self.seq_outs = {t: torch.empty((self.case.batch, sh.num_q_heads, sh.head_dim),
+                                        dtype=TORCH_DTYPE[sh.dtype], device=self.device)
+                         for t in steps}
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for t in steps:
+                self.step_fused(t, out=self.seq_outs[t])
+        torch.cuda.synchronize()
+        self.seq_graph = g
+        return g
+
 
 class DevicePrefill:
     def __init__(self, case, device="cuda:0", poison: bool = True, scheduled: bool = True):

@@ -118,6 +118,17 @@ class _Device:
         assert t in self.graphs
         self._launch("graph", t)
 
+    def capture_sequence(self, steps):
+        steps = list(steps)
+        dev = self
+
+        class _SeqGraph:
+            def replay(self):
+                for t in steps:
+                    dev._launch("graph_seq", t)
+        self.seq_graph, self.seq_outs = _SeqGraph(), {t: None for t in steps}
+        return self.seq_graph
+
 
 def _tiny_case(nsteps=50, batch=3):
     shape = SimpleNamespace(block_size=16, num_blocks=8, num_kv_heads=2, head_dim=8,
@@ -152,8 +163,8 @@ def test_headline_and_extra_legs_run_for_any_step_count(steps, warmup):
     assert abs(extra["kernel_us_mean"] - 80.0) < 1e-6      # event time / K
     bench.guarded(extra, "c3_forms", bench.extra_c3, _Torch, case, dev)
     assert not [k for k in extra if k.endswith("_error")], extra
-    for key in ("c3_fused_graph_replay_us", "c3_separate_store_us", "c3_separate_decode_us",
-                "c3_fused_cold_us_mean"):
+    for key in ("c3_fused_graph_replay_us", "c3_fused_graph_seq_us", "c3_separate_store_us",
+                "c3_separate_decode_us", "c3_fused_cold_us_mean"):
         assert key in extra
 
 

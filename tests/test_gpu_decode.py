@@ -378,6 +378,29 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(to_host_bits(x).view(np.uint8), to_host_bits(y).view(np.uint8))
 
 
+def test_multi_step_graph_matches_eager():
+    """Six fused steps (split plan, shared workspace) captured into ONE HIP graph, each
+    step writing its own output: every replay, with eager work and synchronisations
+    between replays, reproduces the eager outputs of all six steps and the pool bits."""
+    from paged_kv_cache_319_amd.harness import DeviceDecode, to_host_bits
+    banner("multi-step graph replay")
+    case = decode_config("C3", batch=64, steps=6)
+    eager = DeviceDecode(case)
+    want = [to_host_bits(eager.step_fused(t)).copy() for t in range(6)]
+    g = DeviceDecode(case)
+    g.capture_sequence(range(6))
+    other = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        g.seq_graph.replay()
+        torch.cuda.synchronize()
+        for t in range(6):
+            assert np.array_equal(to_host_bits(g.seq_outs[t]), want[t]), f"replay {rep} step {t}"
+        other.mul_(1.0001)                          # eager work between replays
+        torch.cuda.synchronize()
+    for x, y in ((eager.kc, g.kc), (eager.vc, g.vc)):
+        assert np.array_equal(to_host_bits(x).view(np.uint8), to_host_bits(y).view(np.uint8))
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0])
 def test_decode_negative_and_zero_scale(scale):
     """Scores take the caller's scale as given: a negative one reverses the weighting and

@@ -364,13 +364,37 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   if (nchunks <= 1) return;
   const int d = threadIdx.x;
   const int64_t base = (static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_chunks;
-  float M = -INFINITY;
-  for (int cc = 0; cc < nchunks; ++cc) M = fmaxf(M, a.ws_ml[(base + cc) * 2]);
-  float S = 0.f, O = 0.f;
-  for (int cc = 0; cc < nchunks; ++cc) {
-    const float w = __builtin_amdgcn_exp2f(a.ws_ml[(base + cc) * 2] - M);
-    S = fmaf(w, a.ws_ml[(base + cc) * 2 + 1], S);
-    O = fmaf(w, a.ws_o[(base + cc) * D + d], O);
+  // Groups of up to eight chunks: every load of a group is issued before any arithmetic
+  // (one memory round trip per group), then the group's maximum, the rescale of the sums
+  // so far (by 0 on the first group) and the weighted sums in chunk order.
+  constexpr int kGroup = 8;
+  float M = -INFINITY, S = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < nchunks; c0 += kGroup) {
+    float m[kGroup], l[kGroup], o[kGroup];
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int cc = min(c0 + j, nchunks - 1);
+      const bool live = c0 + j < nchunks;
+      const float mv = a.ws_ml[(base + cc) * 2];
+      const float lv = a.ws_ml[(base + cc) * 2 + 1];
+      const float ov = a.ws_o[(base + cc) * D + d];
+      m[j] = live ? mv : -INFINITY;
+      l[j] = live ? lv : 0.f;
+      o[j] = live ? ov : 0.f;
+    }
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) Mg = fmaxf(Mg, m[j]);
+    const float r = __builtin_amdgcn_exp2f(M - Mg);   // M = -inf on the first group: 0
+    S *= r;
+    O *= r;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float w = __builtin_amdgcn_exp2f(m[j] - Mg);
+      S = fmaf(w, l[j], S);
+      O = fmaf(w, o[j], O);
+    }
+    M = Mg;
   }
   store_out<DT>(static_cast<T*>(a.out) + (static_cast<int64_t>(b) * a.num_q_heads + h) * D + d,
                 O / S);
